@@ -1,0 +1,144 @@
+"""Thin ctypes binding of libpa_fp8.so (the C ABI in include/pa_fp8.h).
+
+Argument marshalling only: shapes are read off the torch tensors, pointers
+and sizes are passed through, and every step of the decode runs in the HIP
+library.  There is no fallback: if the library is missing or the tensors are
+not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpa_fp8.so")
+
+PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
+
+EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug",
+           "pa_fp8_last_error", "pa_fp8_version")
+
+
+class PaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pa_fp8 status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load the built library (never builds, never falls back)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with fp8_paged_kv_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        gqa = [P] * 9 + [I] * 6 + [F] + [I] * 4 + [P, Z]
+        L.pa_fp8_decode.argtypes = gqa + [P]
+        L.pa_fp8_decode.restype = I
+        L.pa_fp8_decode_debug.argtypes = gqa + [P, P, P]
+        L.pa_fp8_decode_debug.restype = I
+        L.pa_fp8_decode_workspace_size.argtypes = [I] * 9 + [P, P]
+        L.pa_fp8_decode_workspace_size.restype = I
+        L.pa_fp8_last_error.argtypes = []
+        L.pa_fp8_last_error.restype = ctypes.c_char_p
+        L.pa_fp8_version.argtypes = []
+        L.pa_fp8_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != PA_OK:
+        raise PaError(rc, lib().pa_fp8_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_size(B, s1, nq, nkv, D, block_size, max_blocks_per_seq, s2_tile, num_splits=0):
+    """(bytes, splits) the decode needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    s = ctypes.c_int(0)
+    _check(lib().pa_fp8_decode_workspace_size(B, s1, nq, nkv, D, block_size, max_blocks_per_seq, s2_tile,
+                                              num_splits, ctypes.byref(n), ctypes.byref(s)))
+    return n.value, s.value
+
+
+def _shapes(q, k_cache, block_table, kv_act_seqs, s1):
+    B = int(kv_act_seqs.shape[0])
+    nq, D = int(q.shape[1]), int(q.shape[2])
+    num_blocks, block_size, nkv = int(k_cache.shape[0]), int(k_cache.shape[1]), int(k_cache.shape[2])
+    if s1 is None:
+        if q.shape[0] % B:
+            raise ValueError("q rows are not a multiple of the batch size")
+        s1 = int(q.shape[0]) // B          # [P1] kernel signature: s1 = (B*S1) // B
+    return B, s1, nq, nkv, D, block_size, num_blocks, int(block_table.shape[1])
+
+
+def _checked_inputs(ts):
+    for name, t in ts.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def decode(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_seqs, softmax_scale,
+           s2_tile, num_splits=0, out=None, workspace=None, stream=None, s1=None):
+    """FP8 paged decode; returns out [B*s1, nq, D] bf16 (allocated if not given)."""
+    B, s1, nq, nkv, D, bs, nblk, mbps = _shapes(q, k_cache, block_table, kv_act_seqs, s1)
+    _checked_inputs(dict(q=q, q_scale=q_scale, k_cache=k_cache, k_scale=k_scale, v_cache=v_cache,
+                         v_scale=v_scale, block_table=block_table, kv_act_seqs=kv_act_seqs, out=out,
+                         workspace=workspace))
+    if out is None:
+        out = torch.empty((B * s1, nq, D), dtype=torch.bfloat16, device=q.device)
+    need, _ = workspace_size(B, s1, nq, nkv, D, bs, mbps, s2_tile, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_fp8_decode(
+        _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+        _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),
+        int(s2_tile), mbps, nblk, int(num_splits), _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def decode_debug(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_seqs, softmax_scale,
+                 s2_tile, num_splits=0, stream=None, s1=None):
+    """decode plus the in-kernel dumps: (out, rows [B, max_blocks*block_size] int32, q8 codes)."""
+    B, s1, nq, nkv, D, bs, nblk, mbps = _shapes(q, k_cache, block_table, kv_act_seqs, s1)
+    _checked_inputs(dict(q=q, k_cache=k_cache, block_table=block_table, kv_act_seqs=kv_act_seqs))
+    out = torch.empty((B * s1, nq, D), dtype=torch.bfloat16, device=q.device)
+    rows = torch.empty((B, mbps * bs), dtype=torch.int32, device=q.device)
+    q8 = torch.zeros((B * s1, nq, D), dtype=torch.uint8, device=q.device)
+    need, _ = workspace_size(B, s1, nq, nkv, D, bs, mbps, s2_tile, num_splits)
+    workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    _check(lib().pa_fp8_decode_debug(
+        _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+        _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),
+        int(s2_tile), mbps, nblk, int(num_splits), _ptr(workspace), need, _ptr(rows), _ptr(q8),
+        _stream(stream)))
+    return out, rows, q8
+
+
+def decode_inputs(inp: dict, num_splits=0, out=None, workspace=None, stream=None):
+    """decode() on a dict produced by fp8_paged_kv_amd.synth.make_gqa_inputs."""
+    return decode(inp["q"], inp["q_scale"], inp["k_cache"], inp["k_scale"], inp["v_cache"], inp["v_scale"],
+                  inp["block_table"], inp["kv_act_seqs"], inp["softmax_scale"],
+                  inp.get("s2_tile", inp["cfg"].s2_tile), num_splits=num_splits, out=out, workspace=workspace,
+                  stream=stream, s1=inp["cfg"].s1)

@@ -1,0 +1,192 @@
+// Host side of the C ABI declared in include/pa_fp8.h: argument validation,
+// split planning, workspace sizing and launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pa_fp8.h"
+#include "pa_fp8_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pa_status_t fail(pa_status_t code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool tile_supported(int t) { return t == 128 || t == 256 || t == 512 || t == 1024 || t == 2048; }
+
+// Shape rules shared by every GQA entry point.
+pa_status_t check_shapes(int B, int s1, int nq, int nkv, int D, int block_size, int max_blocks,
+                         int s2_tile, int num_splits) {
+    if (B <= 0 || s1 <= 0 || nq <= 0 || nkv <= 0 || D <= 0 || block_size <= 0 || max_blocks <= 0 ||
+        s2_tile <= 0)
+        return fail(PA_ERR_INVALID, "sizes must be positive (B=%d s1=%d nq=%d nkv=%d D=%d block_size=%d "
+                    "max_blocks_per_seq=%d s2_tile=%d)", B, s1, nq, nkv, D, block_size, max_blocks, s2_tile);
+    if (nq % nkv != 0)
+        return fail(PA_ERR_INVALID, "nq (%d) must be a multiple of nkv (%d)", nq, nkv);
+    if (s2_tile % block_size != 0)
+        return fail(PA_ERR_INVALID, "s2_tile (%d) must be a multiple of block_size (%d)", s2_tile, block_size);
+    if (num_splits < 0)
+        return fail(PA_ERR_INVALID, "num_splits (%d) must be >= 0", num_splits);
+    if (D != pa::kHeadDim)
+        return fail(PA_ERR_UNSUPPORTED, "head dim %d not built (only 128)", D);
+    if (block_size != pa::kBlock)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (only 128)", block_size);
+    if (!tile_supported(s2_tile))
+        return fail(PA_ERR_UNSUPPORTED, "s2_tile %d not built (128, 256, 512, 1024, 2048)", s2_tile);
+    if ((int64_t)s1 * (nq / nkv) > 64)
+        return fail(PA_ERR_UNSUPPORTED, "s1 * nq / nkv = %lld query rows per KV head exceeds 64",
+                    (long long)s1 * (nq / nkv));
+    if ((int64_t)max_blocks * block_size > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size exceeds 2^30 tokens");
+    if ((int64_t)B * s1 * nq > ((int64_t)1 << 31) / 128)
+        return fail(PA_ERR_UNSUPPORTED, "B * s1 * nq too large");
+    return PA_OK;
+}
+
+// Number of contiguous tile ranges per sequence.  The host never reads device
+// memory, so the choice uses the capacity (table row length), not the actual
+// lengths: splits beyond a sequence exit at once.  Aim for enough workgroups
+// to keep every CU streaming.
+int plan_splits(int B, int nkv, int max_tiles, int requested) {
+    if (requested > 0) return requested < max_tiles ? requested : max_tiles;
+    const int64_t units = (int64_t)B * nkv;
+    const int64_t target = 2048;                  // launched workgroups to aim for
+    int64_t s = (target + units - 1) / units;
+    if (s < 1) s = 1;
+    if (s > max_tiles) s = max_tiles;
+    return (int)s;
+}
+
+size_t workspace_bytes_for(int B, int s1, int nq, int nsplit) {
+    if (nsplit <= 1) return 0;
+    const size_t rows = (size_t)B * s1 * nq;
+    const size_t o = rows * nsplit * pa::kHeadDim * sizeof(float);
+    const size_t ml = rows * nsplit * 2 * sizeof(float);
+    return ((o + 255) / 256) * 256 + ml;
+}
+
+pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, const float* k_scale,
+                const uint8_t* v_cache, const float* v_scale, const int32_t* block_table,
+                const int32_t* seqs, void* out, int B, int s1, int nq, int nkv, int D, int block_size,
+                float softmax_scale, int s2_tile, int max_blocks, int num_blocks, int num_splits,
+                void* workspace, size_t workspace_bytes, int32_t* rows_dev, uint8_t* q8_dev,
+                bool debug, void* stream) {
+    g_err[0] = 0;
+    if (!q || !q_scale || !k_cache || !k_scale || !v_cache || !v_scale || !block_table || !seqs || !out)
+        return fail(PA_ERR_NULLPTR, "a required tensor pointer is NULL");
+    if (debug && (!rows_dev || !q8_dev))
+        return fail(PA_ERR_NULLPTR, "debug dump pointers must not be NULL");
+    pa_status_t st = check_shapes(B, s1, nq, nkv, D, block_size, max_blocks, s2_tile, num_splits);
+    if (st != PA_OK) return st;
+    if (num_blocks <= 0) return fail(PA_ERR_INVALID, "num_blocks (%d) must be positive", num_blocks);
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+        return fail(PA_ERR_INVALID, "softmax_scale must be finite and > 0");
+
+    const int capacity = max_blocks * block_size;
+    const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
+    const int nsplit = plan_splits(B, nkv, max_tiles, num_splits);
+    const int tps = (max_tiles + nsplit - 1) / nsplit;
+    const size_t need = workspace_bytes_for(B, s1, nq, nsplit);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)", need, nsplit,
+                    workspace ? workspace_bytes : (size_t)0);
+    if ((int64_t)B * nsplit * nkv > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "grid too large");
+
+    pa::DecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = static_cast<const uint16_t*>(q);
+    p.q_scale = q_scale;
+    p.k_cache = k_cache;
+    p.k_scale = k_scale;
+    p.v_cache = v_cache;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.seqs = seqs;
+    p.out = static_cast<uint16_t*>(out);
+    if (need > 0) {
+        const size_t rows = (size_t)B * s1 * nq;
+        const size_t o = rows * nsplit * pa::kHeadDim * sizeof(float);
+        p.part_o = static_cast<float*>(workspace);
+        p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o + 255) / 256) * 256);
+    }
+    p.dbg_rows = debug ? rows_dev : nullptr;
+    p.dbg_q8 = debug ? q8_dev : nullptr;
+    p.B = B;
+    p.s1 = s1;
+    p.nq = nq;
+    p.nkv = nkv;
+    p.G = nq / nkv;
+    p.rows = s1 * (nq / nkv);
+    p.s2_tile = s2_tile;
+    p.max_blocks = max_blocks;
+    p.num_blocks = num_blocks;
+    p.capacity = capacity;
+    p.nsplit = nsplit;
+    p.tiles_per_split = tps;
+    p.softmax_scale = softmax_scale;
+
+    const hipError_t e = pa::launch_decode(p, static_cast<hipStream_t>(stream), debug);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, int block_size,
+                                         int max_blocks_per_seq, int s2_tile, int num_splits,
+                                         size_t* bytes_host, int* splits_host) {
+    g_err[0] = 0;
+    if (!bytes_host) return fail(PA_ERR_NULLPTR, "bytes_host is NULL");
+    pa_status_t st = check_shapes(B, s1, nq, nkv, D, block_size, max_blocks_per_seq, s2_tile, num_splits);
+    if (st != PA_OK) return st;
+    const int capacity = max_blocks_per_seq * block_size;
+    const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
+    const int nsplit = plan_splits(B, nkv, max_tiles, num_splits);
+    *bytes_host = workspace_bytes_for(B, s1, nq, nsplit);
+    if (splits_host) *splits_host = nsplit;
+    return PA_OK;
+}
+
+pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
+                          const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,
+                          const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev, void* out_dev, int B,
+                          int s1, int nq, int nkv, int D, int block_size, float softmax_scale, int s2_tile,
+                          int max_blocks_per_seq, int num_blocks, int num_splits, void* workspace_dev,
+                          size_t workspace_bytes, void* stream) {
+    return run(q_dev, q_scale_dev, k_cache_dev, k_scale_dev, v_cache_dev, v_scale_dev, block_table_dev,
+               kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
+               max_blocks_per_seq, num_blocks, num_splits, workspace_dev, workspace_bytes, nullptr, nullptr,
+               false, stream);
+}
+
+pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
+                                const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,
+                                const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev, void* out_dev,
+                                int B, int s1, int nq, int nkv, int D, int block_size, float softmax_scale,
+                                int s2_tile, int max_blocks_per_seq, int num_blocks, int num_splits,
+                                void* workspace_dev, size_t workspace_bytes, int32_t* rows_dev, uint8_t* q8_dev,
+                                void* stream) {
+    return run(q_dev, q_scale_dev, k_cache_dev, k_scale_dev, v_cache_dev, v_scale_dev, block_table_dev,
+               kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
+               max_blocks_per_seq, num_blocks, num_splits, workspace_dev, workspace_bytes, rows_dev, q8_dev,
+               true, stream);
+}
+
+const char* pa_fp8_last_error(void) { return g_err; }
+
+const char* pa_fp8_version(void) { return "pa_fp8 0.1 gfx950"; }
+
+}  // extern "C"

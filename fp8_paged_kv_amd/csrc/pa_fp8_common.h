@@ -1,0 +1,35 @@
+// Shared host/device definitions of the HIP decode library (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kHeadDim = 128;   // D of the GQA path
+constexpr int kBlock = 128;     // tokens per cache block
+
+// Everything a decode launch needs; filled and validated on the host.
+struct DecodeParams {
+    const uint16_t* q;          // [B*s1, nq, 128] bf16
+    const float* q_scale;       // [B*s1, nq]
+    const uint8_t* k_cache;     // [num_blocks, 128, nkv, 128]
+    const float* k_scale;       // [num_blocks, 128, nkv]
+    const uint8_t* v_cache;     // [num_blocks, 128, nkv, 128]
+    const float* v_scale;       // [B, nkv, 128]
+    const int32_t* block_table; // [B, max_blocks]
+    const int32_t* seqs;        // [B]
+    uint16_t* out;              // [B*s1, nq, 128] bf16
+    float* part_o;              // [B*s1*nq, nsplit, 128]   (nsplit > 1)
+    float* part_ml;             // [B*s1*nq, nsplit, 2]     (M in log2 units, L)
+    int32_t* dbg_rows;          // [B, capacity] or null
+    uint8_t* dbg_q8;            // [B*s1, nq, 128] or null
+    int B, s1, nq, nkv, G, rows;
+    int s2_tile, max_blocks, num_blocks, capacity;
+    int nsplit, tiles_per_split;
+    float softmax_scale;
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, bool debug);
+
+}  // namespace pa

@@ -1,0 +1,526 @@
+// FP8 paged GQA decode for MI355X (gfx950, CDNA4, wave64).
+//
+// Operation: web page "PyPTO 实现 GLM-4.5 Paged Attention FP8 量化算子分页 KV Cache 与
+// E4M3 混合精度 Kernel 实战解析" (m.nxbn.cn/news/52221), section 计算流程 steps 1-10,
+// section 循环结构 (tiles of s2_tile over the actual length), section 注意事项
+// (block table rules).  The page's own loop nest and tiling target another
+// machine; this file keeps only the arithmetic.
+//
+// Work decomposition (one launch, plus a combine launch when splits > 1):
+//   workgroup  = (batch b, split sp, KV head h); NW waves.
+//   split sp   = tiles [sp*tps, (sp+1)*tps) of the sequence (s2_tile aligned,
+//                so every P-quantisation tile is processed whole).
+//   wave w     = tokens [w*TW, (w+1)*TW) of every tile (TW = 64 or 128).
+//   chunk      = 32 consecutive tokens (one MFMA K-step of P.V); a chunk never
+//                straddles a 128-token block.
+// Per tile each wave computes S^T = K . Q^T for its chunks with the 16x16x128
+// FP8 MFMA (A = 16 tokens x 128 dims of K, loaded straight from HBM with
+// 16-byte loads; B = the FP8 query rows kept in registers).  The S^T layout
+// leaves every lane with 8 tokens of ONE query row, which is exactly the
+// A-operand layout of the 16x16x32 FP8 MFMA used for P.V, so P never moves
+// between lanes.  The tile's row max is exchanged through LDS (one barrier
+// per tile), then P = exp2(S - m_tile) is quantised to FP8 (448 * P) in
+// registers and multiplied with V.  V rows are channel-contiguous, so each
+// lane loads 8-byte pieces of 8 token rows and transposes the 8x8 bytes in
+// registers with v_perm_b32; the output column of MFMA c is d = 8*n + c.
+//
+// Numerics: S is kept in the log2 domain (scaled by log2 e) so exp is
+// v_exp_f32.  The P-quant scale of a tile is max P / 448 = exp(m_tile - M_new)
+// / 448, so the FP8 weights are E4M3(448 * exp(S - m_tile)) and the tile adds
+// exp(m_tile - M_new) / 448 * (P8 . V) to the accumulator; v_scale is a
+// per-channel constant of (b, h) and is applied once at the end.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_fp8_common.h"
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 4x4 byte transpose: out[c] byte k = in[k] byte c.
+__device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                           uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
+    const uint32_t e0 = perm(b, a, 0x06020400u);   // a0 b0 a2 b2
+    const uint32_t e1 = perm(b, a, 0x07030501u);   // a1 b1 a3 b3
+    const uint32_t f0 = perm(d, c, 0x06020400u);   // c0 d0 c2 d2
+    const uint32_t f1 = perm(d, c, 0x07030501u);   // c1 d1 c3 d3
+    o0 = perm(f0, e0, 0x05040100u);                // a0 b0 c0 d0
+    o1 = perm(f1, e1, 0x05040100u);                // a1 b1 c1 d1
+    o2 = perm(f0, e0, 0x07060302u);                // a2 b2 c2 d2
+    o3 = perm(f1, e1, 0x07060302u);                // a3 b3 c3 d3
+}
+
+// Four FP32 values to four E4M3 codes (RNE, no clamp), byte i = value i.
+__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Broadcast lane n of every 16-lane row to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_max_over_groups(float v) {
+    // max over lanes {l, l^16, l^32, l^48}
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_over_groups(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Workgroup id -> logical item such that consecutive logical items run on the
+// same XCD (workgroups are dealt round-robin over the 8 XCDs): the KV heads of
+// one (batch, split) then share that XCD's L2 for the interleaved k_scale lines.
+__device__ __forceinline__ int xcd_swizzle(int x, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int xcd = x & 7, pos = x >> 3;
+    const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    return base + pos;
+}
+
+// token of k-slot (lane group g, byte j) inside a 32-token chunk; equals the
+// token held in element i of MFMA block k of the S^T accumulator (j = 4k + i)
+__device__ __forceinline__ int chunk_token(int g, int j) {
+    return (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <int NRB, int NW, int CPW, bool DBG>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
+    constexpr int TW = CPW * 32;          // tokens per wave per tile
+    constexpr int T = NW * TW;            // s2_tile
+    constexpr int R = NRB * 16;           // padded query rows per KV head
+
+    __shared__ float s_max[2][NW][R];     // per-wave row max of a tile (double-buffered by tile parity)
+    __shared__ float s_acc[R][kHeadDim];  // cross-wave reduction of O
+    __shared__ float s_l[R];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+
+    int item = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int h = item % a.nkv;
+    item /= a.nkv;
+    const int sp = item % a.nsplit;
+    const int b = item / a.nsplit;
+
+    int seq = a.seqs[b];
+    seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
+    const int ntiles = (seq + T - 1) / T;
+    const int t_begin = sp * a.tiles_per_split;
+    const int t_end = min(t_begin + a.tiles_per_split, ntiles);
+
+    if (seq == 0) {
+        // [P1]: nothing to attend to; the rows of this (b, h) are zero.
+        if (a.nsplit == 1) {
+            for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
+                const int r = e / kHeadDim, d = e % kHeadDim;
+                const int s = r / a.G, gq = r % a.G;
+                const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
+                a.out[qrow * kHeadDim + d] = 0;
+            }
+        }
+        if (!DBG || sp != 0) return;
+    } else if (t_begin >= t_end) {
+        return;                           // split beyond this sequence (uniform)
+    }
+
+    // ---- step 1: query rows of this KV head -> FP8 B operand ------------------
+    // lane (lr, lg) holds row rb*16+lr, dims [16lg, 16lg+16) and [64+16lg, 64+16lg+16).
+    i32x8 qop[NRB];
+    float qcoef[NRB];                     // q_scale * softmax_scale * log2 e for row lr
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const int r = rb * 16 + lr;
+        uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        qcoef[rb] = 0.f;
+        if (r < a.rows) {
+            const int s = r / a.G, gq = r % a.G;
+            const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
+            const float qs = a.q_scale[qrow];
+            qcoef[rb] = qs * a.softmax_scale * kLog2e;
+            const uint16_t* qp = a.q + qrow * kHeadDim;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int d0 = half * 64 + 16 * lg;
+                const i32x4 v0 = *reinterpret_cast<const i32x4*>(qp + d0);
+                const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + d0 + 8);
+                uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
+                                   (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
+                float x[16];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    x[2 * i] = bf16_to_f32((uint16_t)(raw[i] & 0xffffu));
+                    x[2 * i + 1] = bf16_to_f32((uint16_t)(raw[i] >> 16));
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    // IEEE divide (as the codes are decided in FP32), then saturate:
+                    // the gfx950 convert rounds to nearest even but does not clamp.
+                    const float y = (qs == 0.f) ? 0.f : x[i] / qs;
+                    x[i] = __builtin_amdgcn_fmed3f(y, -448.f, 448.f);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    wds[half * 4 + i] = cvt4_fp8(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+            }
+            if (DBG && sp == 0 && w == 0 && a.dbg_q8) {
+                uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<uint32_t*>(dst + half * 64 + 16 * lg + 4 * i) = wds[half * 4 + i];
+            }
+        }
+        qop[rb] = i32x8{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3],
+                        (int)wds[4], (int)wds[5], (int)wds[6], (int)wds[7]};
+    }
+    if (seq == 0) return;                 // debug dump of Q only
+
+    const int64_t tok_stride = (int64_t)a.nkv * kHeadDim;      // bytes between tokens of one head
+    const uint8_t* kbase = a.k_cache + (int64_t)h * kHeadDim;
+    const uint8_t* vbase = a.v_cache + (int64_t)h * kHeadDim;
+    const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks;
+
+    // running state; M in the S^T-row layout (row lr) and in the O layout (rows 4lg+i)
+    float M_s[NRB], L_s[NRB];
+    float M_o[NRB][4];
+    f32x4 O[NRB][8];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        M_s[rb] = -INFINITY;
+        L_s[rb] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M_o[rb][i] = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) O[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int t = t_begin; t < t_end; ++t) {
+        const int wlo = t * T + w * TW;
+        float sv[NRB][CPW][8];
+        float rmax[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) rmax[rb] = -INFINITY;
+
+        // ---- steps 2-4: gather K, S^T = K Q^T, dequantise, mask ------------------
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int p0 = wlo + c * 32;
+            if (p0 < seq) {
+                int id = trow[p0 / kBlock];
+                id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+                const int64_t slot0 = (int64_t)id * kBlock + (p0 % kBlock);
+                i32x8 kop[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const uint8_t* kp = kbase + (slot0 + 16 * k + lr) * tok_stride + 16 * lg;
+                    const i32x4 lo = *reinterpret_cast<const i32x4*>(kp);
+                    const i32x4 hi = *reinterpret_cast<const i32x4*>(kp + 64);
+                    kop[k] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    if (DBG && a.dbg_rows && h == 0 && lg == 0 && p0 + 16 * k + lr < seq)
+                        a.dbg_rows[(int64_t)b * a.capacity + p0 + 16 * k + lr] = (int32_t)(slot0 + 16 * k + lr);
+                }
+                const float ksl = a.k_scale[(slot0 + chunk_token(lg, lr & 7)) * a.nkv + h];
+                float ks[8];
+                ks[0] = row_bcast<0>(ksl); ks[1] = row_bcast<1>(ksl);
+                ks[2] = row_bcast<2>(ksl); ks[3] = row_bcast<3>(ksl);
+                ks[4] = row_bcast<4>(ksl); ks[5] = row_bcast<5>(ksl);
+                ks[6] = row_bcast<6>(ksl); ks[7] = row_bcast<7>(ksl);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop[k], qop[rb], acc, 0, 0,
+                                                                               0, 127, 0, 127);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = 4 * k + i;
+                            const bool valid = p0 + chunk_token(lg, j) < seq;
+                            const float sx = acc[i] * ks[j] * qcoef[rb];
+                            sv[rb][c][j] = valid ? sx : -INFINITY;
+                            rmax[rb] = fmaxf(rmax[rb], sv[rb][c][j]);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sv[rb][c][j] = -INFINITY;
+            }
+        }
+
+        // ---- step 5a: tile max per row across lanes and waves ----------------------
+        const int par = t & 1;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            const float m = wave_max_over_groups(rmax[rb]);
+            if (lg == 0) s_max[par][w][rb * 16 + lr] = m;
+        }
+        __syncthreads();
+        float mt_s[NRB], mt_o[NRB][4];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            float m = -INFINITY;
+            float mo[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                m = fmaxf(m, s_max[par][ww][rb * 16 + lr]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mo[i] = fmaxf(mo[i], s_max[par][ww][rb * 16 + 4 * lg + i]);
+            }
+            mt_s[rb] = m;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt_o[rb][i] = mo[i];
+        }
+
+        // ---- steps 5b-7: P, per-tile FP8 quantisation, P.V --------------------------
+        f32x4 Ot[NRB][8];
+        float lsum[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            lsum[rb] = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) Ot[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int p0 = wlo + c * 32;
+            if (p0 < seq) {
+                int id = trow[p0 / kBlock];
+                id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+                const int64_t slot0 = (int64_t)id * kBlock + (p0 % kBlock);
+                uint32_t xl[8], xh[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint8_t* vp = vbase + (slot0 + chunk_token(lg, j)) * tok_stride + 8 * lr;
+                    const uint2 v = *reinterpret_cast<const uint2*>(vp);
+                    xl[j] = v.x;
+                    xh[j] = v.y;
+                }
+                if (p0 + 32 > seq) {
+                    // tokens past the sequence: zero their V bytes (0 * NaN would poison P.V)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const bool valid = p0 + chunk_token(lg, j) < seq;
+                        xl[j] = valid ? xl[j] : 0u;
+                        xh[j] = valid ? xh[j] : 0u;
+                    }
+                }
+                uint32_t ylo[8], yhi[8];
+                transpose4(xl[0], xl[1], xl[2], xl[3], ylo[0], ylo[1], ylo[2], ylo[3]);
+                transpose4(xl[4], xl[5], xl[6], xl[7], yhi[0], yhi[1], yhi[2], yhi[3]);
+                transpose4(xh[0], xh[1], xh[2], xh[3], ylo[4], ylo[5], ylo[6], ylo[7]);
+                transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    float p[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        p[j] = __builtin_amdgcn_exp2f(sv[rb][c][j] - mt_s[rb]);
+                        lsum[rb] += p[j];
+                    }
+                    const uint32_t lo = cvt4_fp8(448.f * p[0], 448.f * p[1], 448.f * p[2], 448.f * p[3]);
+                    const uint32_t hi = cvt4_fp8(448.f * p[4], 448.f * p[5], 448.f * p[6], 448.f * p[7]);
+                    const long pa8 = (long)(((uint64_t)hi << 32) | lo);
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc) {
+                        const long vb = (long)(((uint64_t)yhi[cc] << 32) | ylo[cc]);
+                        Ot[rb][cc] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pa8, vb, Ot[rb][cc], 0, 0, 0);
+                    }
+                }
+            }
+        }
+
+        // ---- steps 8-9: rescale and accumulate ------------------------------------
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            const float mn = fmaxf(M_s[rb], mt_s[rb]);
+            L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) + lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
+            M_s[rb] = mn;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mo = fmaxf(M_o[rb][i], mt_o[rb][i]);
+                const float al = __builtin_amdgcn_exp2f(M_o[rb][i] - mo);
+                const float be = __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
+                M_o[rb][i] = mo;
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] = O[rb][cc][i] * al + Ot[rb][cc][i] * be;
+            }
+        }
+    }
+
+    // ---- cross-wave reduction (fixed order w = 0, 1, ...) --------------------------
+    float Lw[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) Lw[rb] = wave_sum_over_groups(L_s[rb]);
+    for (int ww = 0; ww < NW; ++ww) {
+        if (w == ww) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float* dst = &s_acc[rb * 16 + 4 * lg + i][8 * lr];
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc) dst[cc] = (ww == 0) ? O[rb][cc][i] : dst[cc] + O[rb][cc][i];
+                }
+                if (lg == 0) s_l[rb * 16 + lr] = (ww == 0) ? Lw[rb] : s_l[rb * 16 + lr] + Lw[rb];
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- step 10 (or partials for the combine) ----------------------------------------
+    const float* vs = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim;
+    for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
+        const int r = e / kHeadDim, d = e % kHeadDim;
+        const int s = r / a.G, gq = r % a.G;
+        const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
+        const float o = s_acc[r][d];
+        if (a.nsplit == 1) {
+            const float val = o * vs[d] / (448.f * s_l[r]);
+            a.out[qrow * kHeadDim + d] = f32_to_bf16_rne(val);
+        } else {
+            a.part_o[(qrow * a.nsplit + sp) * kHeadDim + d] = o;
+        }
+    }
+    if (a.nsplit > 1) {
+        // M of the row (any lane with that S^T row holds it; every wave has it)
+        if (w == 0 && lg == 0) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const int r = rb * 16 + lr;
+                if (r < a.rows) {
+                    const int s = r / a.G, gq = r % a.G;
+                    const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
+                    a.part_ml[(qrow * a.nsplit + sp) * 2 + 0] = M_s[rb];
+                    a.part_ml[(qrow * a.nsplit + sp) * 2 + 1] = s_l[r];
+                }
+            }
+        }
+    }
+}
+
+// One wave per output row: log-sum-exp merge of the split partials in split order.
+__global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t qrow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nrows = (int64_t)a.B * a.s1 * a.nq;
+    if (qrow >= nrows) return;
+    const int b = (int)(qrow / ((int64_t)a.s1 * a.nq));
+    const int qh = (int)(qrow % a.nq);
+    const int h = qh / a.G;
+    int seq = a.seqs[b];
+    seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
+    const int T = a.s2_tile;
+    const int ntiles = (seq + T - 1) / T;
+    const int nact = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+    const float* ml = a.part_ml + qrow * a.nsplit * 2;
+    float Ms = -INFINITY;
+    for (int i = 0; i < nact; ++i) Ms = fmaxf(Ms, ml[2 * i]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int i = 0; i < nact; ++i) {
+        const float f = __builtin_amdgcn_exp2f(ml[2 * i] - Ms);
+        L += ml[2 * i + 1] * f;
+        const float2 o = *reinterpret_cast<const float2*>(a.part_o + (qrow * a.nsplit + i) * kHeadDim + 2 * lane);
+        o0 += o.x * f;
+        o1 += o.y * f;
+    }
+    const float* vs = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim;
+    uint16_t r0 = 0, r1 = 0;
+    if (nact > 0) {
+        r0 = f32_to_bf16_rne(o0 * vs[2 * lane] / (448.f * L));
+        r1 = f32_to_bf16_rne(o1 * vs[2 * lane + 1] / (448.f * L));
+    }
+    *reinterpret_cast<uint32_t*>(a.out + qrow * kHeadDim + 2 * lane) = (uint32_t)r0 | ((uint32_t)r1 << 16);
+}
+
+// Fill an int32 buffer (debug dump of gathered rows).
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <int NRB, int NW, int CPW>
+static hipError_t launch_nrb(const DecodeParams& p, int grid, hipStream_t st, bool dbg) {
+    if (dbg)
+        hipLaunchKernelGGL((decode_kernel<NRB, NW, CPW, true>), dim3(grid), dim3(NW * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<NRB, NW, CPW, false>), dim3(grid), dim3(NW * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int NW, int CPW>
+static hipError_t launch_tile(const DecodeParams& p, int nrb, int grid, hipStream_t st, bool dbg) {
+    switch (nrb) {
+        case 1: return launch_nrb<1, NW, CPW>(p, grid, st, dbg);
+        case 2: return launch_nrb<2, NW, CPW>(p, grid, st, dbg);
+        case 3: return launch_nrb<3, NW, CPW>(p, grid, st, dbg);
+        default: return launch_nrb<4, NW, CPW>(p, grid, st, dbg);
+    }
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t st, bool dbg) {
+    const int nrb = (p.rows + 15) / 16;
+    const int grid = p.B * p.nsplit * p.nkv;
+    hipError_t e;
+    if (dbg && p.dbg_rows) {
+        const int64_t n = (int64_t)p.B * p.capacity;
+        hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
+                           dim3(256), 0, st, p.dbg_rows, n, -1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    switch (p.s2_tile) {
+        case 128: e = launch_tile<2, 2>(p, nrb, grid, st, dbg); break;
+        case 256: e = launch_tile<4, 2>(p, nrb, grid, st, dbg); break;
+        case 512: e = launch_tile<4, 4>(p, nrb, grid, st, dbg); break;
+        case 1024: e = launch_tile<8, 4>(p, nrb, grid, st, dbg); break;
+        default: e = launch_tile<16, 4>(p, nrb, grid, st, dbg); break;
+    }
+    if (e != hipSuccess) return e;
+    if (p.nsplit > 1) {
+        const int64_t nrows = (int64_t)p.B * p.s1 * p.nq;
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, p);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace pa

@@ -1,0 +1,136 @@
+/*
+ * pa_fp8.h — C ABI of the MI355X (gfx950) FP8 paged-attention decode library.
+ *
+ * Sources (web pages; cited by title and section):
+ * [P1] "PyPTO 实现 GLM-4.5 Paged Attention FP8 量化算子分页 KV Cache 与 E4M3 混合精度
+ *      Kernel 实战解析" (m.nxbn.cn/news/52221) — the decode operation:
+ *      section 计算流程 (the ten computation steps), section Kernel 签名
+ *      (tensor shapes and dtypes), section 量化策略 (scale rules),
+ *      section 注意事项 (block-table and sequence-length rules).
+ * [P2] "PyPTO-Gym 算子实战DeepSeek V32 MLA 的 Sparse Attention FP8 反量化算子"
+ *      (www.mhpn.cn/news/2272720) — the MLA sparse variant: section
+ *      核心参数与 KV Cache 布局 (672-byte rows), section API 签名 (tensors),
+ *      section 计算流程 (gather, dequant, attention).
+ * [P3] "CANN ops-transformer aclnnKvCompressEpilog 算子详解" (www.lmnt.cn/news/267091)
+ *      — the two-phase convention (query the workspace size, then run with
+ *      a caller-owned workspace) and distinct null-pointer / invalid-argument
+ *      status codes.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev are device pointers (HBM of the current device);
+ *    pointers named *_host are host pointers.  Tensors are dense row-major.
+ *  - The caller owns every buffer.  The library allocates nothing, frees
+ *    nothing and never synchronises the stream; work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the null stream) and returns immediately.
+ *  - Inputs are read only.  Outputs are written completely.  The workspace
+ *    is scratch whose contents are undefined after the call.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is launched and a status != PA_OK is returned, with a
+ *    message available from pa_fp8_last_error() (per host thread).
+ *  - Scales are dequantisation multipliers (amax / 448): a value is
+ *    code_value * scale.  [P1] stores 448 / amax and dequantises with its
+ *    reciprocal; the two are the same scale.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef PA_FP8_H
+#define PA_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int pa_status_t;
+enum {
+    PA_OK = 0,
+    PA_ERR_NULLPTR = 1,      /* a required pointer is NULL                       */
+    PA_ERR_INVALID = 2,      /* a shape or scalar violates the operation's rules */
+    PA_ERR_UNSUPPORTED = 3,  /* legal in principle but not built (e.g. D != 128) */
+    PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required          */
+    PA_ERR_HIP = 5           /* the HIP runtime reported an error at launch      */
+};
+
+/*
+ * Workspace bytes pa_fp8_decode needs for these sizes and split count
+ * (num_splits 0 = the library's choice, the same one pa_fp8_decode makes).
+ * Writes the size to *bytes_host (0 when no workspace is needed) and, when
+ * splits_host is not NULL, the split count that will be used.
+ */
+pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, int block_size,
+                                         int max_blocks_per_seq, int s2_tile, int num_splits,
+                                         size_t* bytes_host, int* splits_host);
+
+/*
+ * FP8 paged GQA decode, [P1] section 计算流程 steps 1-10.  For every batch b,
+ * query position s < s1 and query head qh (served by KV head h = qh / (nq/nkv),
+ * contiguous groups):
+ *   1  q8 = E4M3(q / q_scale) (round to nearest even, saturate at +-448);
+ *   2  the tokens p < seq_b are read through block_table in tiles of s2_tile;
+ *   3  S_raw = q8 . k8 (FP8 MFMA, FP32 accumulate);
+ *   4  S = S_raw * q_scale * k_scale[p] * softmax_scale;
+ *   5  running max M, running sum L += sum exp(S - M) (unquantised);
+ *   6  per row and tile: P8 = E4M3(P * 448 / max_tile P);
+ *   7  O_tile = P8 . v8 (FP8 MFMA);
+ *   8-9 O = O * exp(M_old - M_new) + O_tile * (max_tile P / 448) * v_scale;
+ *   10 out = bf16(O / L).
+ * Layouts:
+ *   q_dev            [B*s1, nq, D]                  bf16
+ *   q_scale_dev      [B*s1, nq]                     fp32, per query token and head
+ *   k_cache_dev      [num_blocks, block_size, nkv, D] OCP e4m3fn codes
+ *   k_scale_dev      [num_blocks, block_size, nkv]  fp32, per token and KV head
+ *   v_cache_dev      [num_blocks, block_size, nkv, D] OCP e4m3fn codes
+ *   v_scale_dev      [B, nkv, D]                    fp32, per batch, KV head and channel
+ *   block_table_dev  [B, max_blocks_per_seq]        int32 physical block ids
+ *   kv_act_seqs_dev  [B]                            int32 valid tokens per batch
+ *   out_dev          [B*s1, nq, D]                  bf16, written completely
+ * Device-side rules ([P1] section 注意事项): only table entries that cover
+ * tokens p < seq_b are read; an entry < 0 or >= num_blocks reads block 0
+ * (the page clamps -1 to 0); seq_b is clamped to
+ * [0, max_blocks_per_seq * block_size]; seq_b == 0 gives zero output rows;
+ * bytes of tokens p >= seq_b are never used (their values may be NaN).
+ * Supported: D == 128, block_size == 128, s2_tile in {128, 256, 512, 1024,
+ * 2048}, s1 * nq / nkv <= 64.  num_splits: 0 = auto, else the number of
+ * contiguous tile ranges each sequence is split into (>= 1); splits > 1
+ * need the workspace from pa_fp8_decode_workspace_size.
+ */
+pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev,
+                          const uint8_t* k_cache_dev, const float* k_scale_dev,
+                          const uint8_t* v_cache_dev, const float* v_scale_dev,
+                          const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
+                          void* out_dev,
+                          int B, int s1, int nq, int nkv, int D, int block_size,
+                          float softmax_scale, int s2_tile, int max_blocks_per_seq, int num_blocks,
+                          int num_splits, void* workspace_dev, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * pa_fp8_decode plus two dumps taken from inside the kernel:
+ *   rows_dev [B, max_blocks_per_seq * block_size] int32: for every logical
+ *            token p < seq_b the physical token row (block_id * block_size +
+ *            p % block_size) whose K was read; -1 for every other position.
+ *   q8_dev   [B*s1, nq, D] uint8: the FP8 query codes of step 1.
+ * Same arguments, rules and return codes as pa_fp8_decode.
+ */
+pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev,
+                                const uint8_t* k_cache_dev, const float* k_scale_dev,
+                                const uint8_t* v_cache_dev, const float* v_scale_dev,
+                                const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
+                                void* out_dev,
+                                int B, int s1, int nq, int nkv, int D, int block_size,
+                                float softmax_scale, int s2_tile, int max_blocks_per_seq, int num_blocks,
+                                int num_splits, void* workspace_dev, size_t workspace_bytes,
+                                int32_t* rows_dev, uint8_t* q8_dev, void* stream);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* pa_fp8_last_error(void);
+
+/* Library version string, e.g. "pa_fp8 0.1 gfx950". */
+const char* pa_fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_FP8_H */

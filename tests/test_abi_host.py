@@ -1,0 +1,76 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared
+entry point, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa_fp8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_fp8_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp8_paged_kv_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from fp8_paged_kv_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_expected_entry_points():
+    from fp8_paged_kv_amd import binding
+    assert set(declared_functions()) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert lib.pa_fp8_version().decode().startswith("pa_fp8")
+
+
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+
+
+def call(lib, **over):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, v=FAKE, vs=FAKE, table=FAKE, seqs=FAKE, out=FAKE,
+             B=2, s1=1, nq=8, nkv=2, D=128, bs=128, scale=0.088, tile=256, mbps=6, nblocks=8, splits=1,
+             ws=None, wsb=0, stream=None)
+    a.update(over)
+    return lib.pa_fp8_decode(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["table"], a["seqs"], a["out"],
+                             a["B"], a["s1"], a["nq"], a["nkv"], a["D"], a["bs"], a["scale"], a["tile"],
+                             a["mbps"], a["nblocks"], a["splits"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(table=None), 1),
+    (dict(B=0), 2), (dict(nq=7), 2), (dict(tile=200), 2), (dict(splits=-1), 2), (dict(nblocks=0), 2),
+    (dict(scale=0.0), 2), (dict(scale=float("inf")), 2), (dict(scale=float("nan")), 2),
+    (dict(D=64), 3), (dict(bs=64, tile=256), 3), (dict(tile=384), 3), (dict(s1=5, nq=32, nkv=2), 3),
+    (dict(splits=2, ws=None), 4), (dict(splits=2, ws=FAKE, wsb=16), 4),
+])
+def test_host_validation_codes(lib, over, code):
+    assert call(lib, **over) == code
+    assert len(lib.pa_fp8_last_error()) > 0
+
+
+def test_workspace_query(lib):
+    from fp8_paged_kv_amd import binding
+    n, s = binding.workspace_size(2, 1, 8, 2, 128, 128, 6, 256, 1)
+    assert (n, s) == (0, 1)
+    n, s = binding.workspace_size(2, 1, 8, 2, 128, 128, 6, 256, 3)
+    assert s == 3 and n >= 2 * 8 * 3 * (128 * 4 + 8)
+    n, s = binding.workspace_size(4, 1, 96, 8, 128, 128, 1024, 512, 0)
+    assert 1 <= s <= 256 and n > 0
+    with pytest.raises(binding.PaError):
+        binding.workspace_size(2, 1, 8, 3, 128, 128, 6, 256, 1)

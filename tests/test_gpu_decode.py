@@ -1,0 +1,175 @@
+"""GPU parity of the HIP decode against the CPU oracle (through the C ABI).
+
+Every test prints the case it runs before touching the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_paged_kv_amd import synth
+from tests.gpu_util import compare, gpu_out_float, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp8_paged_kv_amd import binding
+    binding.lib()
+    return binding
+
+
+def _case(name, **kw):
+    base = dict(name=name, B=2, s1=1, nq=8, nkv=2, D=128, seq_lens=(200, 513), s2_tile=256,
+                num_blocks=10, max_blocks_per_seq=6, seed=7)
+    base.update(kw)
+    return synth.GqaConfig(**base)
+
+
+def _run(B, inp_h, num_splits=0, tag=""):
+    print(f"[gpu] {tag} cfg={inp_h['cfg'].name} splits={num_splits} "
+          f"seqs={inp_h['kv_act_seqs'].tolist()[:8]}", flush=True)
+    d = to_device(inp_h)
+    out = B.decode_inputs(d, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return gpu_out_float(out)
+
+
+def test_config0_parity(B, oracle_mod):
+    inp = synth.make_gqa_inputs(synth.CONFIGS[0])
+    ref = oracle_mod.gqa_decode(inp)
+    for ns in (0, 1, 2, 3):
+        got = _run(B, inp, ns, "config0")
+        compare(got, ref["out_bf16"], f"config0 splits={ns}")
+
+
+def test_config0_gather_and_q_codes_bit_exact(B, oracle_mod):
+    inp = synth.make_gqa_inputs(synth.CONFIGS[0])
+    ref = oracle_mod.gqa_decode(inp)
+    print("[gpu] config0 debug dump", flush=True)
+    d = to_device(inp)
+    out, rows, q8 = B.decode_debug(d["q"], d["q_scale"], d["k_cache"], d["k_scale"], d["v_cache"],
+                                   d["v_scale"], d["block_table"], d["kv_act_seqs"], d["softmax_scale"],
+                                   inp["cfg"].s2_tile)
+    torch.cuda.synchronize()
+    assert np.array_equal(rows.cpu().numpy(), ref["rows"])
+    assert np.array_equal(q8.cpu().numpy(), ref["q8"])
+    compare(gpu_out_float(out), ref["out_bf16"], "config0 debug")
+
+
+@pytest.mark.parametrize("s2_tile", [128, 256, 512, 1024, 2048])
+def test_tile_sizes(B, oracle_mod, s2_tile):
+    cfg = _case(f"tile{s2_tile}", seq_lens=(1, 127, 129, 1500, 2048, 2100), B=6, nq=8, nkv=2,
+                num_blocks=64, max_blocks_per_seq=17, s2_tile=s2_tile, seed=s2_tile)
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    for ns in (1, 0, 5):
+        compare(_run(B, inp, ns, f"tile{s2_tile}"), ref["out_bf16"], f"s2_tile={s2_tile} splits={ns}")
+
+
+@pytest.mark.parametrize("s1,nq,nkv", [(1, 12, 1), (1, 96, 8), (2, 48, 8), (4, 32, 4), (3, 48, 3),
+                                        (4, 64, 4), (1, 16, 16), (1, 64, 1)])
+def test_row_shapes(B, oracle_mod, s1, nq, nkv):
+    # rows per KV head = s1 * nq / nkv: 12, 12, 12, 32, 48, 64, 1, 64
+    cfg = _case(f"rows-s1{s1}-nq{nq}-nkv{nkv}", B=3, s1=s1, nq=nq, nkv=nkv, seq_lens=(77, 600, 1100),
+                num_blocks=20, max_blocks_per_seq=9, s2_tile=256, seed=nq + s1)
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    for ns in (0, 1, 4):
+        compare(_run(B, inp, ns, "rows"), ref["out_bf16"], f"s1={s1} nq={nq} nkv={nkv} splits={ns}")
+
+
+def test_edge_lengths(B, oracle_mod):
+    # empty sequence, length 1, exact tile / block multiples, ragged tails, a full row
+    cfg = _case("edges", B=8, seq_lens=(0, 1, 128, 256, 257, 511, 512, 768), num_blocks=40,
+                max_blocks_per_seq=6, s2_tile=256, seed=3)
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    for ns in (1, 2, 3, 0):
+        got = _run(B, inp, ns, "edges")
+        compare(got, ref["out_bf16"], f"edges splits={ns}")
+        assert np.all(got.reshape(8, 8, 128)[0] == 0.0)
+
+
+def test_clamped_length_and_bad_ids(B, oracle_mod):
+    cfg = _case("clamp", B=2, seq_lens=(300, 700), num_blocks=12, max_blocks_per_seq=6, seed=4)
+    inp = synth.make_gqa_inputs(cfg)
+    inp["kv_act_seqs"] = torch.tensor([300, 10 ** 6], dtype=torch.int32)     # clamped to 768
+    t = inp["block_table"].clone()
+    t[1, 5] = -1                                # inside the clamped length: reads block 0
+    t[0, 1] = 10 ** 7                           # out of range: reads block 0
+    inp["block_table"] = t
+    ref = oracle_mod.gqa_decode(inp)
+    for ns in (1, 0):
+        compare(_run(B, inp, ns, "clamp"), ref["out_bf16"], f"clamp splits={ns}")
+
+
+def test_poison_beyond_sequence_bit_identical(B):
+    cfg = _case("poison", B=4, seq_lens=(1, 200, 513, 1000), num_blocks=20, max_blocks_per_seq=8, seed=9)
+    clean = _run(B, synth.make_gqa_inputs(cfg), 0, "poison-clean")
+    dirty_inp = synth.make_gqa_inputs(cfg, poison=True)
+    assert torch.isnan(dirty_inp["k_scale"]).any()
+    dirty = _run(B, dirty_inp, 0, "poison-dirty")
+    assert np.array_equal(clean, dirty)
+
+
+def test_block_relabelling_bit_identical(B):
+    cfg = _case("relabel", B=3, seq_lens=(100, 700, 1300), num_blocks=24, max_blocks_per_seq=11, seed=10)
+    inp = synth.make_gqa_inputs(cfg)
+    base = _run(B, inp, 0, "relabel-base")
+    perm = torch.randperm(cfg.num_blocks, generator=torch.Generator().manual_seed(1))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(cfg.num_blocks)
+    t = inp["block_table"].clone()
+    t[t >= 0] = inv[t[t >= 0].long()].to(torch.int32)
+    moved = dict(inp, k_cache=inp["k_cache"][perm].contiguous(), v_cache=inp["v_cache"][perm].contiguous(),
+                 k_scale=inp["k_scale"][perm].contiguous(), block_table=t)
+    assert np.array_equal(base, _run(B, moved, 0, "relabel-moved"))
+
+
+def test_deterministic_repeat(B):
+    cfg = _case("repeat", B=4, seq_lens=(900, 20, 3000, 1), num_blocks=40, max_blocks_per_seq=24, seed=12)
+    inp = synth.make_gqa_inputs(cfg)
+    a = _run(B, inp, 0, "repeat-1")
+    b = _run(B, inp, 0, "repeat-2")
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 3])
+def test_scaled_down_configs_full_parity(B, oracle_mod, cfg_id):
+    # the full-size shapes with fewer sequences, every output row checked
+    from dataclasses import replace
+    full = synth.CONFIGS[cfg_id]
+    cfg = replace(full, B=4 if cfg_id == 1 else 16, num_blocks=full.max_blocks_per_seq * (4 if cfg_id == 1 else 16))
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    for ns in (0, 1):
+        compare(_run(B, inp, ns, f"config{cfg_id}-small"), ref["out_bf16"], f"config{cfg_id} small splits={ns}")
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3])
+def test_full_size_configs_sampled_rows(B, oracle_mod, cfg_id):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    recomputes a sample of output rows one by one."""
+    cfg = synth.CONFIGS[cfg_id]
+    print(f"[gpu] full-size config {cfg_id} generating on GPU", flush=True)
+    inp_d = synth.make_gqa_inputs(cfg, device="cuda")
+    out = _run_dev(B, inp_d, f"config{cfg_id}-full")
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp_d.items()}
+    nrows = cfg.B * cfg.s1 * cfg.nq
+    g = np.random.default_rng(cfg_id)
+    rows = np.unique(np.concatenate([[0, nrows - 1], g.choice(nrows, 46, replace=False)]))
+    ref = oracle_mod.gqa_decode_rows(host, rows)
+    got = out.reshape(nrows, cfg.D)[rows]
+    compare(got, ref["out_bf16"], f"config{cfg_id} full sampled rows")
+
+
+def _run_dev(B, inp_d, tag, num_splits=0):
+    print(f"[gpu] {tag} splits={num_splits}", flush=True)
+    out = B.decode_inputs(inp_d, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return gpu_out_float(out)
