@@ -1,0 +1,225 @@
+"""Benchmark: FP8 paged GQA decode on one MI355X.
+
+One step = one decode call (pa_fp8_decode: every step of the path, through
+the C ABI) over one batch of synthetic input already resident in HBM.  The
+workload is the GLM-4.5-shaped decode (B=32, nq=96, nkv=8, D=128, block 128,
+lengths U[1024, 8192], s2_tile 512).  Timed steps rotate over several
+independent input sets (>= 1 GB together) so the 256 MB Infinity Cache
+cannot serve them; a warm-cache figure (one set repeated) is printed too.
+
+Prints ONE JSON line.  `value` is achieved GB/s of algorithmic bytes (K, V,
+k_scale of every valid token and KV head, v_scale, Q, q_scale, output, the
+table entries and lengths) per decode call.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "fp8_paged_kv_amd", "csrc", "pa_fp8_decode.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_glm45_config1_pmc.md")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA)")
+    ap.add_argument("--splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled by the timed steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-target-s", type=float, default=15.0, help="wall seconds budget of the oracle sample")
+    ap.add_argument("--pmc-mode", action="store_true",
+                    help="short fixed run for counter collection: decode calls plus a plain copy of known size")
+    ap.add_argument("--sweep-splits", type=str, default="", help="comma list; prints one line per split count")
+    return ap.parse_args()
+
+
+def make_sets(cfg, n, device="cuda"):
+    from fp8_paged_kv_amd import synth
+    first = synth.make_gqa_inputs(cfg, device=device)
+    seqs = first["kv_act_seqs"].cpu().tolist()
+    sets = [first]
+    for i in range(1, n):
+        sets.append(synth.make_gqa_inputs(cfg, device=device, seed=1000 + 17 * i + cfg.seed, seq_lens=seqs))
+    return sets, seqs
+
+
+def time_calls(binding, sets, steps, warmup, splits, out, ws):
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        binding.decode_inputs(sets[i % len(sets)], num_splits=splits, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        binding.decode_inputs(sets[i % len(sets)], num_splits=splits, out=out, workspace=ws, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))     # ms per call, on the launch stream
+    return wall, ev
+
+
+def cpu_baseline(cfg, sets, seqs, target_s):
+    """The oracle as it stands, on the first sequences of the same workload."""
+    import numpy as np
+    from fp8_paged_kv_amd import synth
+    from oracle import oracle
+    host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in sets[0].items()}
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = max(1, min(threads, 16))          # one GPU's share of the host
+    # calibrate on one sequence, then size the sample to the time budget
+    t0 = time.perf_counter()
+    oracle.gqa_decode(host, b_range=(0, 1), threads=1)
+    one = time.perf_counter() - t0
+    per_tok = one / max(1, seqs[0])
+    nb, acc = 0, 0.0
+    for s in seqs:
+        if nb > 0 and acc + per_tok * s / threads > target_s:
+            break
+        acc += per_tok * s / threads
+        nb += 1
+    used = min(threads, nb)
+    t0 = time.perf_counter()
+    oracle.gqa_decode(host, b_range=(0, nb), threads=used)
+    dt = time.perf_counter() - t0
+    sub = synth.GqaConfig(**{**cfg.__dict__, "B": nb})
+    sample_bytes = synth.gqa_algorithmic_bytes(sub, seqs[:nb])
+    full_tokens = sum(seqs)
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"sequences 0..{nb - 1} of {cfg.B} ({sum(seqs[:nb])} of {full_tokens} tokens, all "
+                      f"{cfg.nq} query heads), FP64 C oracle, {dt:.2f} s wall on {used} threads",
+            "calls_per_s_equiv": round((sum(seqs[:nb]) / full_tokens) / dt, 6)}
+
+
+def pmc_traffic():
+    """Counter-measured HBM bytes per decode launch, if the summary matches this kernel."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None, "no counter summary"
+    text = open(PMC_SUMMARY).read()
+    m = re.search(r"kernel_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t:
+        return None, "summary incomplete"
+    if m.group(1) != kernel_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(t.group(1)), "ok"
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from fp8_paged_kv_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    binding.lib()
+    cfg = synth.CONFIGS[args.config]
+    sets, seqs = make_sets(cfg, max(1, args.rotate))
+    nbytes = synth.gqa_algorithmic_bytes(cfg, seqs)
+    kv_bytes = sum(seqs) * cfg.nkv * 2 * cfg.D
+    out = torch.empty((cfg.B * cfg.s1, cfg.nq, cfg.D), dtype=torch.bfloat16, device="cuda")
+
+    def run(splits, steps, warmup, rot):
+        need, nsplit = binding.workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.nkv, cfg.D, cfg.block_size,
+                                              cfg.max_blocks_per_seq, cfg.s2_tile, splits)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        wall, ev = time_calls(binding, rot, steps, warmup, splits, out, ws)
+        return wall, ev, nsplit
+
+    if args.pmc_mode:
+        # fixed, short: decode calls then one plain device copy of known size
+        run(args.splits, 20, 5, sets)
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_mode": True, "decode_calls": 25, "copy_bytes": src.numel(), "copies": 5,
+                          "algorithmic_bytes_per_call": nbytes}))
+        return
+
+    if args.sweep_splits:
+        for sp in [int(x) for x in args.sweep_splits.split(",")]:
+            wall, ev, nsplit = run(sp, args.steps, args.warmup, sets)
+            med = ev[len(ev) // 2]
+            print(json.dumps({"splits": nsplit, "median_us": round(med * 1e3, 2),
+                              "gb_s": round(nbytes / (med * 1e-3) / 1e9, 1),
+                              "wall_us_per_call": round(wall / args.steps * 1e6, 2)}), flush=True)
+        return
+
+    wall, ev, nsplit = run(args.splits, args.steps, args.warmup, sets)
+    ms_per_step = wall / args.steps * 1e3
+    mean_ev = sum(ev) / len(ev)
+    med_ev = ev[len(ev) // 2]
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (mean_ev * 1e-3) / 1e9
+    _, ev_warm, _ = run(args.splits, max(20, args.steps // 4), 5, sets[:1])
+    warm = nbytes / (sum(ev_warm) / len(ev_warm) * 1e-3) / 1e9
+    traffic, traffic_note = pmc_traffic()
+
+    line = {
+        "metric": "achieved HBM GB/s (% of 8 TB/s peak) + decode calls/s, FP8 paged GQA decode",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (products exact, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "s1": cfg.s1, "nq": cfg.nq, "nkv": cfg.nkv, "D": cfg.D,
+                   "block_size": cfg.block_size, "s2_tile": cfg.s2_tile, "seq_lens": "U[1024,8192] seed 1",
+                   "total_tokens": sum(seqs), "splits": nsplit, "rotating_input_sets": len(sets),
+                   "algorithmic_bytes_per_call": nbytes},
+        "calls_per_s": round(1.0 / (ms_per_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_gb_s": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "query_head_tokens_per_s": round(cfg.B * cfg.s1 * cfg.nq / (ms_per_step * 1e-3), 1),
+        "event_us_per_call": {"mean": round(mean_ev * 1e3, 2), "median": round(med_ev * 1e3, 2),
+                              "p10": round(ev[len(ev) // 10] * 1e3, 2), "p90": round(ev[(9 * len(ev)) // 10] * 1e3, 2)},
+        "warm_cache_gb_s": round(warm, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic), "traffic_note": traffic_note,
+                     "kernel": "pa::decode_kernel" + (" + pa::combine_kernel" if nsplit > 1 else "")},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, sets, seqs, args.cpu_target_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
