@@ -151,7 +151,7 @@ def main():
     def run(splits, steps, warmup, rot):
         need, nsplit = binding.workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.nkv, cfg.D, cfg.block_size,
                                               cfg.max_blocks_per_seq, cfg.s2_tile, splits)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
         wall, ev = time_calls(binding, rot, steps, warmup, splits, out, ws)
         return wall, ev, nsplit
 

@@ -109,7 +109,7 @@ def decode(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_s
         out = torch.empty((B * s1, nq, D), dtype=torch.bfloat16, device=q.device)
     need, _ = workspace_size(B, s1, nq, nkv, D, bs, mbps, s2_tile, num_splits)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_fp8_decode(
         _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
@@ -127,7 +127,7 @@ def decode_debug(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv
     rows = torch.empty((B, mbps * bs), dtype=torch.int32, device=q.device)
     q8 = torch.zeros((B * s1, nq, D), dtype=torch.uint8, device=q.device)
     need, _ = workspace_size(B, s1, nq, nkv, D, bs, mbps, s2_tile, num_splits)
-    workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    workspace = torch.zeros(need, dtype=torch.uint8, device=q.device) if need else None
     _check(lib().pa_fp8_decode_debug(
         _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
         _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),

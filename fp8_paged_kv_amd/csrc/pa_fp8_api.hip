@@ -56,23 +56,37 @@ pa_status_t check_shapes(int B, int s1, int nq, int nkv, int D, int block_size, 
 // Number of contiguous tile ranges per sequence.  The host never reads device
 // memory, so the choice uses the capacity (table row length), not the actual
 // lengths: splits beyond a sequence exit at once.  Aim for enough workgroups
-// to keep every CU streaming.
+// to keep every CU streaming; more than one split is rounded to a multiple of
+// 8 (the placement spreads splits over the 8 XCDs).
 int plan_splits(int B, int nkv, int max_tiles, int requested) {
     if (requested > 0) return requested < max_tiles ? requested : max_tiles;
     const int64_t units = (int64_t)B * nkv;
     const int64_t target = 2048;                  // launched workgroups to aim for
     int64_t s = (target + units - 1) / units;
-    if (s < 1) s = 1;
+    if (s <= 1) return 1;
+    s = (s + 7) / 8 * 8;
     if (s > max_tiles) s = max_tiles;
     return (int)s;
 }
 
-size_t workspace_bytes_for(int B, int s1, int nq, int nsplit) {
-    if (nsplit <= 1) return 0;
-    const size_t rows = (size_t)B * s1 * nq;
-    const size_t o = rows * nsplit * pa::kHeadDim * sizeof(float);
-    const size_t ml = rows * nsplit * 2 * sizeof(float);
-    return ((o + 255) / 256) * 256 + ml;
+int rows_pad(int s1, int nq, int nkv) { return (s1 * (nq / nkv) + 15) / 16 * 16; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct WorkspaceLayout {
+    size_t counters, part_ml, part_o, total;
+};
+
+// [B*nkv int32 counters | pad][B*nkv*nsplit*R*2 floats | pad][B*nkv*nsplit*R*128 floats]
+WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit) {
+    WorkspaceLayout l = {0, 0, 0, 0};
+    if (nsplit <= 1) return l;
+    const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
+    l.counters = 0;
+    l.part_ml = align256(units * sizeof(int32_t));
+    l.part_o = l.part_ml + align256(units * nsplit * R * 2 * sizeof(float));
+    l.total = l.part_o + units * nsplit * R * pa::kHeadDim * sizeof(float);
+    return l;
 }
 
 pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, const float* k_scale,
@@ -96,11 +110,13 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
     const int nsplit = plan_splits(B, nkv, max_tiles, num_splits);
     const int tps = (max_tiles + nsplit - 1) / nsplit;
-    const size_t need = workspace_bytes_for(B, s1, nq, nsplit);
+    const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit);
+    const size_t need = lay.total;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)", need, nsplit,
                     workspace ? workspace_bytes : (size_t)0);
-    if ((int64_t)B * nsplit * nkv > 0x7fffffff)
+    const int nsplit_pad = nsplit == 1 ? 1 : (nsplit + 7) / 8 * 8;
+    if ((int64_t)((B + 7) / 8 * 8) * nsplit_pad * nkv > 0x7fffffff)
         return fail(PA_ERR_UNSUPPORTED, "grid too large");
 
     pa::DecodeParams p;
@@ -115,10 +131,10 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.seqs = seqs;
     p.out = static_cast<uint16_t*>(out);
     if (need > 0) {
-        const size_t rows = (size_t)B * s1 * nq;
-        const size_t o = rows * nsplit * pa::kHeadDim * sizeof(float);
-        p.part_o = static_cast<float*>(workspace);
-        p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o + 255) / 256) * 256);
+        char* base = static_cast<char*>(workspace);
+        p.counters = reinterpret_cast<int32_t*>(base + lay.counters);
+        p.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
+        p.part_o = reinterpret_cast<float*>(base + lay.part_o);
     }
     p.dbg_rows = debug ? rows_dev : nullptr;
     p.dbg_q8 = debug ? q8_dev : nullptr;
@@ -133,6 +149,7 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.num_blocks = num_blocks;
     p.capacity = capacity;
     p.nsplit = nsplit;
+    p.nsplit_pad = nsplit_pad;
     p.tiles_per_split = tps;
     p.softmax_scale = softmax_scale;
 
@@ -155,7 +172,7 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
     const int capacity = max_blocks_per_seq * block_size;
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
     const int nsplit = plan_splits(B, nkv, max_tiles, num_splits);
-    *bytes_host = workspace_bytes_for(B, s1, nq, nsplit);
+    *bytes_host = layout_for(B, s1, nq, nkv, nsplit).total;
     if (splits_host) *splits_host = nsplit;
     return PA_OK;
 }

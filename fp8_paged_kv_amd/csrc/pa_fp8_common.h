@@ -20,16 +20,18 @@ struct DecodeParams {
     const int32_t* block_table; // [B, max_blocks]
     const int32_t* seqs;        // [B]
     uint16_t* out;              // [B*s1, nq, 128] bf16
-    float* part_o;              // [B*s1*nq, nsplit, 128]   (nsplit > 1)
-    float* part_ml;             // [B*s1*nq, nsplit, 2]     (M in log2 units, L)
+    int32_t* counters;          // [B*nkv] arrival counters (zero between calls)  (nsplit > 1)
+    float* part_o;              // [B*nkv, nsplit, rows_pad, 128]
+    float* part_ml;             // [B*nkv, nsplit, rows_pad, 2]  (M in log2 units, L)
     int32_t* dbg_rows;          // [B, capacity] or null
     uint8_t* dbg_q8;            // [B*s1, nq, 128] or null
     int B, s1, nq, nkv, G, rows;
     int s2_tile, max_blocks, num_blocks, capacity;
-    int nsplit, tiles_per_split;
+    int nsplit, nsplit_pad, tiles_per_split;
     float softmax_scale;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, bool debug);
+int grid_size(const DecodeParams& p);
 
 }  // namespace pa

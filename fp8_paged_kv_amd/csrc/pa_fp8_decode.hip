@@ -6,8 +6,11 @@
 // (block table rules).  The page's own loop nest and tiling target another
 // machine; this file keeps only the arithmetic.
 //
-// Work decomposition (one launch, plus a combine launch when splits > 1):
-//   workgroup  = (batch b, split sp, KV head h); NW waves.
+// Work decomposition (one launch):
+//   workgroup  = (batch b, split sp, KV head h); NW waves.  With several
+//                splits holding work, each writes (O, M, L) partials and the
+//                last one to finish (an arrival counter per (b, h) in the
+//                workspace, left at zero again) merges them in split order.
 //   split sp   = tiles [sp*tps, (sp+1)*tps) of the sequence (s2_tile aligned,
 //                so every P-quantisation tile is processed whole).
 //   wave w     = tokens [w*TW, (w+1)*TW) of every tile (TW = 64 or 128).
@@ -49,6 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2_448 = 8.807354922057604f;   // log2(448)
 
 // ---------------------------------------------------------------- helpers
 
@@ -126,14 +130,34 @@ __device__ __forceinline__ float wave_sum_over_groups(float v) {
     return v;
 }
 
-// Workgroup id -> logical item such that consecutive logical items run on the
-// same XCD (workgroups are dealt round-robin over the 8 XCDs): the KV heads of
-// one (batch, split) then share that XCD's L2 for the interleaved k_scale lines.
-__device__ __forceinline__ int xcd_swizzle(int x, int n) {
-    const int q = n >> 3, r = n & 7;
+// Workgroup placement.  Workgroups are dealt round-robin over the 8 XCDs
+// (id x runs on XCD x % 8), each XCD with its own L2.  A work unit is a
+// (batch b, split sp); its nkv heads get consecutive ids on ONE XCD, so the
+// k_scale lines they share ([token][kv head] interleaved) are fetched from
+// HBM once.  Units are spread over XCDs by (b + sp) % 8 so every die gets a
+// mix of short and long sequences.  The id space is padded (splits to a
+// multiple of 8, or batches to a multiple of 8 without splits); padded ids
+// are empty.
+struct Placement {
+    int b, sp, h;
+    bool empty;
+};
+
+__device__ __forceinline__ Placement place(int x, int B, int nsplit, int nsplit_pad, int nkv) {
+    Placement r;
     const int xcd = x & 7, pos = x >> 3;
-    const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-    return base + pos;
+    r.h = pos % nkv;
+    const int q = pos / nkv;
+    if (nsplit_pad == 1) {
+        r.b = q * 8 + xcd;
+        r.sp = 0;
+    } else {
+        const int per = nsplit_pad >> 3;
+        r.b = q / per;
+        r.sp = 8 * (q % per) + ((xcd - r.b) & 7);
+    }
+    r.empty = r.b >= B || r.sp >= nsplit;
+    return r;
 }
 
 // token of k-slot (lane group g, byte j) inside a 32-token chunk; equals the
@@ -144,26 +168,41 @@ __device__ __forceinline__ int chunk_token(int g, int j) {
 
 // ------------------------------------------------------------------ kernel
 
+// ------------------------------------------------------------------ kernel
+
+constexpr int kRing = 4;                  // register ring of chunk buffers (3 in flight)
+constexpr float kDropLog2 = 40.f;         // tiles 2^40 below the running max are dropped
+
+// One prefetched chunk: 16 dwords of K (two 16-token blocks x 32 bytes) or of
+// V (8 tokens x 8 bytes), plus the lane's k_scale word for K chunks.
+struct Chunk {
+    uint32_t w[16];
+    float ks;
+};
+
 template <int NRB, int NW, int CPW, bool DBG>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 2 : 1)))
+void decode_kernel(DecodeParams a) {
     constexpr int TW = CPW * 32;          // tokens per wave per tile
     constexpr int T = NW * TW;            // s2_tile
     constexpr int R = NRB * 16;           // padded query rows per KV head
+    constexpr int STEPS = 2 * CPW;        // chunk steps per tile: CPW of K, then CPW of V
+    static_assert(STEPS % kRing == 0, "ring must divide the steps of a tile");
 
     __shared__ float s_max[2][NW][R];     // per-wave row max of a tile (double-buffered by tile parity)
-    __shared__ float s_acc[R][kHeadDim];  // cross-wave reduction of O
+    __shared__ float s_acc[R][kHeadDim];  // cross-wave reduction of O (also the combine's staging)
     __shared__ float s_l[R];
+    __shared__ float s_ms[R];
+    __shared__ int s_last;
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, made scalar
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
-    int item = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int h = item % a.nkv;
-    item /= a.nkv;
-    const int sp = item % a.nsplit;
-    const int b = item / a.nsplit;
+    const Placement pl = place(blockIdx.x, a.B, a.nsplit, a.nsplit_pad, a.nkv);
+    if (pl.empty) return;
+    const int b = pl.b, sp = pl.sp, h = pl.h;
 
     int seq = a.seqs[b];
     seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
@@ -172,8 +211,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
     const int t_end = min(t_begin + a.tiles_per_split, ntiles);
 
     if (seq == 0) {
-        // [P1]: nothing to attend to; the rows of this (b, h) are zero.
-        if (a.nsplit == 1) {
+        // nothing to attend to: the rows of this (b, h) are zero
+        if (sp == 0) {
             for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
                 const int r = e / kHeadDim, d = e % kHeadDim;
                 const int s = r / a.G, gq = r % a.G;
@@ -186,7 +225,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
         return;                           // split beyond this sequence (uniform)
     }
 
-    // ---- step 1: query rows of this KV head -> FP8 B operand ------------------
+    // ---- step 1: query rows of this KV head -> bf16 operands of exact FP8 values --------
     // lane (lr, lg) holds row rb*16+lr, dims [16lg, 16lg+16) and [64+16lg, 64+16lg+16).
     bf16x8 qop[NRB][4];                   // operand i: codes [8i, 8i+8) of the lane's 32
     float qcoef[NRB];                     // q_scale * softmax_scale * log2 e for row lr
@@ -216,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    // IEEE divide (as the codes are decided in FP32), then saturate:
+                    // IEEE divide (the codes are decided in FP32), then saturate:
                     // the gfx950 convert rounds to nearest even but does not clamp.
                     const float y = (qs == 0.f) ? 0.f : x[i] / qs;
                     x[i] = __builtin_amdgcn_fmed3f(y, -448.f, 448.f);
@@ -244,6 +283,58 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
     const uint8_t* vbase = a.v_cache + (int64_t)h * kHeadDim;
     const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks;
 
+    // First physical token row of chunk c of tile t for this wave, or -1 when
+    // the chunk holds no valid token.  A chunk never straddles a block.  All
+    // of it is wave-uniform (scalar registers).
+    auto chunk_slot = [&](int t, int c) -> int64_t {
+        const int p0 = t * T + w * TW + 32 * c;
+        if (t >= t_end || p0 >= seq) return -1;
+        int id = trow[p0 / kBlock];
+        id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+        return (int64_t)id * kBlock + (p0 % kBlock);
+    };
+    // Per-lane byte offsets inside a chunk (constant over the loop): K rows
+    // 16k + lr at bytes 16lg and 64 + 16lg; V rows chunk_token(lg, j) at byte
+    // 8lr; the k_scale word of token chunk_token(lg, lr & 7).
+    uint32_t koff[2], voff[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) koff[k] = (uint32_t)((16 * k + lr) * tok_stride + 16 * lg);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) voff[j] = (uint32_t)(chunk_token(lg, j) * tok_stride + 8 * lr);
+    const uint32_t ksoff = (uint32_t)(chunk_token(lg, lr & 7) * a.nkv * 4);
+    const uint8_t* ksbase = reinterpret_cast<const uint8_t*>(a.k_scale + h);
+
+    // Issue the loads of step u (static) of tile t into ring slot `ch`.  Chunks
+    // without valid tokens load block 0's first rows instead (always in
+    // bounds, L2-resident, never used), which keeps the code straight-line.
+    auto issue = [&](Chunk& ch, int t, int u) {
+        const int c = u < CPW ? u : u - CPW;
+        int64_t s0 = chunk_slot(t, c);
+        s0 = s0 < 0 ? 0 : s0;
+        if (u < CPW) {
+            const uint8_t* kb = kbase + s0 * tok_stride;              // uniform base
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + koff[k]);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + koff[k] + 64);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ch.w[8 * k + i] = (uint32_t)lo[i];
+                    ch.w[8 * k + 4 + i] = (uint32_t)hi[i];
+                }
+            }
+            ch.ks = *reinterpret_cast<const float*>(ksbase + s0 * a.nkv * 4 + ksoff);
+        } else {
+            const uint8_t* vb = vbase + s0 * tok_stride;              // uniform base
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint2 v = *reinterpret_cast<const uint2*>(vb + voff[j]);
+                ch.w[2 * j] = v.x;
+                ch.w[2 * j + 1] = v.y;
+            }
+        }
+    };
+
     // running state; M in the S^T-row layout (row lr) and in the O layout (rows 4lg+i)
     float M_s[NRB], L_s[NRB];
     float M_o[NRB][4];
@@ -258,173 +349,188 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
         for (int c = 0; c < 8; ++c) O[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    Chunk ring[kRing];
+#pragma unroll
+    for (int u = 0; u < kRing - 1; ++u) issue(ring[u], t_begin, u);
+
     for (int t = t_begin; t < t_end; ++t) {
         const int wlo = t * T + w * TW;
         float sv[NRB][CPW][8];
         float rmax[NRB];
+        float mt_s[NRB], mt_o[NRB][4];
+        float lsum[NRB];
+        float poff[NRB];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) rmax[rb] = -INFINITY;
+        for (int rb = 0; rb < NRB; ++rb) {
+            rmax[rb] = -INFINITY;
+            lsum[rb] = 0.f;
+        }
 
-        // ---- steps 2-4: gather K, S^T = K Q^T, dequantise, mask ------------------
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int p0 = wlo + c * 32;
-            if (p0 < seq) {
-                int id = trow[p0 / kBlock];
-                id = (id < 0 || id >= a.num_blocks) ? 0 : id;
-                const int64_t slot0 = (int64_t)id * kBlock + (p0 % kBlock);
-                uint32_t kraw[2][8];
+        for (int u = 0; u < STEPS; ++u) {
+            // keep kRing-1 chunks in flight: load step u + kRing - 1 (maybe next tile)
+            {
+                const int un = u + kRing - 1;
+                if (un < STEPS) issue(ring[un % kRing], t, un);
+                else issue(ring[un % kRing], t + 1, un - STEPS);
+            }
+            Chunk& ch = ring[u % kRing];
+            const int c = u < CPW ? u : u - CPW;
+            const int p0 = wlo + 32 * c;
+            const bool valid = p0 < seq;
+
+            if (u < CPW) {
+                // ---- steps 2-4: S^T = K Q^T (exact products, FP32 sums), dequantise, mask
+                if (valid) {
+                    if (DBG && a.dbg_rows && h == 0 && lg == 0) {
+                        const int64_t s0 = chunk_slot(t, c);
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const uint8_t* kp = kbase + (slot0 + 16 * k + lr) * tok_stride + 16 * lg;
-                    const i32x4 lo = *reinterpret_cast<const i32x4*>(kp);
-                    const i32x4 hi = *reinterpret_cast<const i32x4*>(kp + 64);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        kraw[k][i] = (uint32_t)lo[i];
-                        kraw[k][4 + i] = (uint32_t)hi[i];
+                        for (int k = 0; k < 2; ++k)
+                            if (p0 + 16 * k + lr < seq)
+                                a.dbg_rows[(int64_t)b * a.capacity + p0 + 16 * k + lr] = (int32_t)(s0 + 16 * k + lr);
                     }
-                    if (DBG && a.dbg_rows && h == 0 && lg == 0 && p0 + 16 * k + lr < seq)
-                        a.dbg_rows[(int64_t)b * a.capacity + p0 + 16 * k + lr] = (int32_t)(slot0 + 16 * k + lr);
+                    float ks[8];
+                    ks[0] = row_bcast<0>(ch.ks); ks[1] = row_bcast<1>(ch.ks);
+                    ks[2] = row_bcast<2>(ch.ks); ks[3] = row_bcast<3>(ch.ks);
+                    ks[4] = row_bcast<4>(ch.ks); ks[5] = row_bcast<5>(ch.ks);
+                    ks[6] = row_bcast<6>(ch.ks); ks[7] = row_bcast<7>(ch.ks);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        bf16x8 kop[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) kop[i] = fp8x8_to_op(ch.w[8 * k + 2 * i], ch.w[8 * k + 2 * i + 1]);
+#pragma unroll
+                        for (int rb = 0; rb < NRB; ++rb) {
+                            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc = mfma_bf16(kop[i], qop[rb][i], acc);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) sv[rb][c][4 * k + i] = acc[i] * ks[4 * k + i] * qcoef[rb];
+                        }
+                    }
+                    if (p0 + 32 > seq) {
+                        // the sequence ends inside this chunk: mask the tokens past it
+#pragma unroll
+                        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                sv[rb][c][j] = (p0 + chunk_token(lg, j) < seq) ? sv[rb][c][j] : -INFINITY;
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) rmax[rb] = fmaxf(rmax[rb], sv[rb][c][j]);
+                } else {
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) sv[rb][c][j] = -INFINITY;
                 }
-                const float ksl = a.k_scale[(slot0 + chunk_token(lg, lr & 7)) * a.nkv + h];
-                float ks[8];
-                ks[0] = row_bcast<0>(ksl); ks[1] = row_bcast<1>(ksl);
-                ks[2] = row_bcast<2>(ksl); ks[3] = row_bcast<3>(ksl);
-                ks[4] = row_bcast<4>(ksl); ks[5] = row_bcast<5>(ksl);
-                ks[6] = row_bcast<6>(ksl); ks[7] = row_bcast<7>(ksl);
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    bf16x8 kop[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) kop[i] = fp8x8_to_op(kraw[k][2 * i], kraw[k][2 * i + 1]);
+
+                if (u == CPW - 1) {
+                    // ---- step 5a: tile max per row across lanes and waves ------------
+                    const int par = t & 1;
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                        const float m = wave_max_over_groups(rmax[rb]);
+                        if (lg == 0) s_max[par][w][rb * 16 + lr] = m;
+                    }
+                    __syncthreads();
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc = mfma_bf16(kop[i], qop[rb][i], acc);
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        float m = -INFINITY;
+                        float mo[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+                        for (int ww = 0; ww < NW; ++ww) {
+                            m = fmaxf(m, s_max[par][ww][rb * 16 + lr]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) mo[i] = fmaxf(mo[i], s_max[par][ww][rb * 16 + 4 * lg + i]);
+                        }
+                        mt_s[rb] = m;
+                        // exp2 argument offset: P' = 448 * exp2(S - m_tile) = exp2(S + off);
+                        // a dropped row gets off = -inf (P' = 0, nothing added)
+                        poff[rb] = (M_s[rb] - m > kDropLog2) ? -INFINITY : kLog2_448 - m;
+                        // O <- O * exp2(M_old - m_tile): alpha if the tile raises the max,
+                        // else 1/beta; the tile's P.V is then added and the sum scaled by beta.
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int j = 4 * k + i;
-                            const bool valid = p0 + chunk_token(lg, j) < seq;
-                            const float sx = acc[i] * ks[j] * qcoef[rb];
-                            sv[rb][c][j] = valid ? sx : -INFINITY;
-                            rmax[rb] = fmaxf(rmax[rb], sv[rb][c][j]);
+                            mt_o[rb][i] = mo[i];
+                            const float d = M_o[rb][i] - mo[i];
+                            const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(d);
+#pragma unroll
+                            for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
                         }
                     }
                 }
             } else {
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) sv[rb][c][j] = -INFINITY;
-            }
-        }
-
-        // ---- step 5a: tile max per row across lanes and waves ----------------------
-        const int par = t & 1;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            const float m = wave_max_over_groups(rmax[rb]);
-            if (lg == 0) s_max[par][w][rb * 16 + lr] = m;
-        }
-        __syncthreads();
-        float mt_s[NRB], mt_o[NRB][4];
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            float m = -INFINITY;
-            float mo[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                m = fmaxf(m, s_max[par][ww][rb * 16 + lr]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mo[i] = fmaxf(mo[i], s_max[par][ww][rb * 16 + 4 * lg + i]);
-            }
-            mt_s[rb] = m;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mt_o[rb][i] = mo[i];
-        }
-
-        // ---- steps 5b-7: P, per-tile FP8 quantisation, P.V --------------------------
-        f32x4 Ot[NRB][8];
-        float lsum[NRB];
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            lsum[rb] = 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) Ot[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int p0 = wlo + c * 32;
-            if (p0 < seq) {
-                int id = trow[p0 / kBlock];
-                id = (id < 0 || id >= a.num_blocks) ? 0 : id;
-                const int64_t slot0 = (int64_t)id * kBlock + (p0 % kBlock);
-                uint32_t xl[8], xh[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint8_t* vp = vbase + (slot0 + chunk_token(lg, j)) * tok_stride + 8 * lr;
-                    const uint2 v = *reinterpret_cast<const uint2*>(vp);
-                    xl[j] = v.x;
-                    xh[j] = v.y;
-                }
-                if (p0 + 32 > seq) {
-                    // tokens past the sequence: zero their V bytes (0 * NaN would poison P.V)
+                // ---- steps 5b-7: P, per-tile FP8 quantisation, P.V ----------------------
+                if (valid) {
+                    uint32_t xl[8], xh[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const bool valid = p0 + chunk_token(lg, j) < seq;
-                        xl[j] = valid ? xl[j] : 0u;
-                        xh[j] = valid ? xh[j] : 0u;
+                        xl[j] = ch.w[2 * j];
+                        xh[j] = ch.w[2 * j + 1];
+                    }
+                    if (p0 + 32 > seq) {
+                        // tokens past the sequence: zero their V bytes (0 * NaN would poison P.V)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const bool in = p0 + chunk_token(lg, j) < seq;
+                            xl[j] = in ? xl[j] : 0u;
+                            xh[j] = in ? xh[j] : 0u;
+                        }
+                    }
+                    uint32_t ylo[8], yhi[8];
+                    transpose4(xl[0], xl[1], xl[2], xl[3], ylo[0], ylo[1], ylo[2], ylo[3]);
+                    transpose4(xl[4], xl[5], xl[6], xl[7], yhi[0], yhi[1], yhi[2], yhi[3]);
+                    transpose4(xh[0], xh[1], xh[2], xh[3], ylo[4], ylo[5], ylo[6], ylo[7]);
+                    transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
+                    bf16x8 pop[NRB];
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        float p[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            p[j] = __builtin_amdgcn_exp2f(sv[rb][c][j] + poff[rb]);
+                            lsum[rb] += p[j];
+                        }
+                        // step 6: FP8 code of 448 * P (the tile's max P maps to 448), held as bf16
+                        const uint32_t lo = cvt4_fp8(p[0], p[1], p[2], p[3]);
+                        const uint32_t hi = cvt4_fp8(p[4], p[5], p[6], p[7]);
+                        pop[rb] = fp8x8_to_op(lo, hi);
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc) {
+                        const bf16x8 vop = fp8x8_to_op(ylo[cc], yhi[cc]);
+#pragma unroll
+                        for (int rb = 0; rb < NRB; ++rb) O[rb][cc] = mfma_bf16(pop[rb], vop, O[rb][cc]);
                     }
                 }
-                uint32_t ylo[8], yhi[8];
-                transpose4(xl[0], xl[1], xl[2], xl[3], ylo[0], ylo[1], ylo[2], ylo[3]);
-                transpose4(xl[4], xl[5], xl[6], xl[7], yhi[0], yhi[1], yhi[2], yhi[3]);
-                transpose4(xh[0], xh[1], xh[2], xh[3], ylo[4], ylo[5], ylo[6], ylo[7]);
-                transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
-                bf16x8 pop[NRB];
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    float p[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        p[j] = __builtin_amdgcn_exp2f(sv[rb][c][j] - mt_s[rb]);
-                        lsum[rb] += p[j];
-                    }
-                    // step 6: FP8 code of 448 * P (the tile's max P maps to 448), held as bf16
-                    const uint32_t lo = cvt4_fp8(448.f * p[0], 448.f * p[1], 448.f * p[2], 448.f * p[3]);
-                    const uint32_t hi = cvt4_fp8(448.f * p[4], 448.f * p[5], 448.f * p[6], 448.f * p[7]);
-                    pop[rb] = fp8x8_to_op(lo, hi);
-                }
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const bf16x8 vop = fp8x8_to_op(ylo[cc], yhi[cc]);
-#pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) Ot[rb][cc] = mfma_bf16(pop[rb], vop, Ot[rb][cc]);
-                }
-            }
-        }
 
-        // ---- steps 8-9: rescale and accumulate ------------------------------------
+                if (u == STEPS - 1) {
+                    // ---- steps 8-9: finish the rescale, update the running state --------
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            const float mn = fmaxf(M_s[rb], mt_s[rb]);
-            L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) + lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
-            M_s[rb] = mn;
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        const float mn = fmaxf(M_s[rb], mt_s[rb]);
+                        L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) +
+                                  lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
+                        M_s[rb] = mn;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float mo = fmaxf(M_o[rb][i], mt_o[rb][i]);
-                const float al = __builtin_amdgcn_exp2f(M_o[rb][i] - mo);
-                const float be = __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
-                M_o[rb][i] = mo;
+                        for (int i = 0; i < 4; ++i) {
+                            const float mo = fmaxf(M_o[rb][i], mt_o[rb][i]);
+                            const float d = M_o[rb][i] - mt_o[rb][i];
+                            const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
+                            M_o[rb][i] = mo;
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] = O[rb][cc][i] * al + Ot[rb][cc][i] * be;
+                            for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
+                        }
+                    }
+                }
             }
         }
     }
 
-    // ---- cross-wave reduction (fixed order w = 0, 1, ...) --------------------------
+    // ---- cross-wave reduction (fixed order w = 0, 1, ...) --------------------------------
     float Lw[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) Lw[rb] = wave_sum_over_groups(L_s[rb]);
@@ -444,69 +550,68 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams a) {
         __syncthreads();
     }
 
-    // ---- step 10 (or partials for the combine) ----------------------------------------
     const float* vs = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim;
-    for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
-        const int r = e / kHeadDim, d = e % kHeadDim;
-        const int s = r / a.G, gq = r % a.G;
-        const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
-        const float o = s_acc[r][d];
-        if (a.nsplit == 1) {
-            const float val = o * vs[d] / (448.f * s_l[r]);
-            a.out[qrow * kHeadDim + d] = f32_to_bf16_rne(val);
-        } else {
-            a.part_o[(qrow * a.nsplit + sp) * kHeadDim + d] = o;
+    const int nact = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;   // splits with work
+    if (nact == 1) {
+        // ---- step 10: out = O * v_scale / L' (L' = 448 L: P' = 448 P is summed), bf16 ----
+        for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
+            const int r = e / kHeadDim, d = e % kHeadDim;
+            const int s = r / a.G, gq = r % a.G;
+            const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
+            a.out[qrow * kHeadDim + d] = f32_to_bf16_rne(s_acc[r][d] * vs[d] / s_l[r]);
         }
+        return;
     }
-    if (a.nsplit > 1) {
-        // M of the row (any lane with that S^T row holds it; every wave has it)
-        if (w == 0 && lg == 0) {
+
+    // ---- split partials, then the last split of (b, h) merges them -------------------------
+    // partial layout: [b][h][split][R rows][128] for O, [b][h][split][R][2] for (M, L)
+    const int64_t unit = (int64_t)b * a.nkv + h;
+    float* po = a.part_o + (unit * a.nsplit + sp) * (R * kHeadDim);
+    float* pml = a.part_ml + (unit * a.nsplit + sp) * (R * 2);
+    for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) po[e] = s_acc[e / kHeadDim][e % kHeadDim];
+    if (w == 0 && lg == 0) {
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) {
-                const int r = rb * 16 + lr;
-                if (r < a.rows) {
-                    const int s = r / a.G, gq = r % a.G;
-                    const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
-                    a.part_ml[(qrow * a.nsplit + sp) * 2 + 0] = M_s[rb];
-                    a.part_ml[(qrow * a.nsplit + sp) * 2 + 1] = s_l[r];
-                }
+        for (int rb = 0; rb < NRB; ++rb) {
+            const int r = rb * 16 + lr;
+            if (r < a.rows) {
+                pml[2 * r] = M_s[rb];
+                pml[2 * r + 1] = s_l[r];
             }
         }
     }
-}
+    __syncthreads();                      // every partial store of this workgroup is done
+    if (threadIdx.x == 0) {
+        // release our partials, count the arrival (agent scope: splits run on any XCD)
+        const int prev = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == nact - 1);
+        if (s_last) __hip_atomic_store(a.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);
 
-// One wave per output row: log-sum-exp merge of the split partials in split order.
-__global__ __launch_bounds__(256) void combine_kernel(DecodeParams a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t qrow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t nrows = (int64_t)a.B * a.s1 * a.nq;
-    if (qrow >= nrows) return;
-    const int b = (int)(qrow / ((int64_t)a.s1 * a.nq));
-    const int qh = (int)(qrow % a.nq);
-    const int h = qh / a.G;
-    int seq = a.seqs[b];
-    seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
-    const int T = a.s2_tile;
-    const int ntiles = (seq + T - 1) / T;
-    const int nact = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-    const float* ml = a.part_ml + qrow * a.nsplit * 2;
-    float Ms = -INFINITY;
-    for (int i = 0; i < nact; ++i) Ms = fmaxf(Ms, ml[2 * i]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int i = 0; i < nact; ++i) {
-        const float f = __builtin_amdgcn_exp2f(ml[2 * i] - Ms);
-        L += ml[2 * i + 1] * f;
-        const float2 o = *reinterpret_cast<const float2*>(a.part_o + (qrow * a.nsplit + i) * kHeadDim + 2 * lane);
-        o0 += o.x * f;
-        o1 += o.y * f;
+    // log-sum-exp merge of the nact partials, in split order (deterministic)
+    const float* po0 = a.part_o + (unit * a.nsplit) * (R * kHeadDim);
+    const float* pml0 = a.part_ml + (unit * a.nsplit) * (R * 2);
+    for (int r = threadIdx.x; r < a.rows; r += NW * 64) {
+        float Ms = -INFINITY;
+        for (int i = 0; i < nact; ++i) Ms = fmaxf(Ms, pml0[i * R * 2 + 2 * r]);
+        float L = 0.f;
+        for (int i = 0; i < nact; ++i) L += pml0[i * R * 2 + 2 * r + 1] * __builtin_amdgcn_exp2f(pml0[i * R * 2 + 2 * r] - Ms);
+        s_l[r] = L;
+        s_ms[r] = Ms;
     }
-    const float* vs = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim;
-    uint16_t r0 = 0, r1 = 0;
-    if (nact > 0) {
-        r0 = f32_to_bf16_rne(o0 * vs[2 * lane] / (448.f * L));
-        r1 = f32_to_bf16_rne(o1 * vs[2 * lane + 1] / (448.f * L));
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
+        const int r = e / kHeadDim, d = e % kHeadDim;
+        const float Ms = s_ms[r];
+        float o = 0.f;
+        for (int i = 0; i < nact; ++i)
+            o += po0[(int64_t)i * R * kHeadDim + e] * __builtin_amdgcn_exp2f(pml0[i * R * 2 + 2 * r] - Ms);
+        const int s = r / a.G, gq = r % a.G;
+        const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
+        a.out[qrow * kHeadDim + d] = f32_to_bf16_rne(o * vs[d] / s_l[r]);
     }
-    *reinterpret_cast<uint32_t*>(a.out + qrow * kHeadDim + 2 * lane) = (uint32_t)r0 | ((uint32_t)r1 << 16);
 }
 
 // Fill an int32 buffer (debug dump of gathered rows).
@@ -536,9 +641,14 @@ static hipError_t launch_tile(const DecodeParams& p, int nrb, int grid, hipStrea
     }
 }
 
+int grid_size(const DecodeParams& p) {
+    const int bpad = p.nsplit_pad == 1 ? (p.B + 7) / 8 * 8 : p.B;
+    return bpad * p.nsplit_pad * p.nkv;
+}
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st, bool dbg) {
     const int nrb = (p.rows + 15) / 16;
-    const int grid = p.B * p.nsplit * p.nkv;
+    const int grid = grid_size(p);
     hipError_t e;
     if (dbg && p.dbg_rows) {
         const int64_t n = (int64_t)p.B * p.capacity;
@@ -552,12 +662,6 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t st, bool dbg) {
         case 512: e = launch_tile<4, 4>(p, nrb, grid, st, dbg); break;
         case 1024: e = launch_tile<8, 4>(p, nrb, grid, st, dbg); break;
         default: e = launch_tile<16, 4>(p, nrb, grid, st, dbg); break;
-    }
-    if (e != hipSuccess) return e;
-    if (p.nsplit > 1) {
-        const int64_t nrows = (int64_t)p.B * p.s1 * p.nq;
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, p);
-        e = hipGetLastError();
     }
     return e;
 }

@@ -22,8 +22,11 @@
  *  - The caller owns every buffer.  The library allocates nothing, frees
  *    nothing and never synchronises the stream; work is enqueued on `stream`
  *    (a hipStream_t; NULL = the null stream) and returns immediately.
- *  - Inputs are read only.  Outputs are written completely.  The workspace
- *    is scratch whose contents are undefined after the call.
+ *  - Inputs are read only.  Outputs are written completely.
+ *  - Workspace (only when a call splits sequences): its first bytes hold one
+ *    arrival counter per (batch, KV head).  They must be zero before the
+ *    first call that uses the buffer (e.g. allocate it zero-filled); every
+ *    call leaves them zero again.  The rest is scratch.
  *  - Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and a status != PA_OK is returned, with a
  *    message available from pa_fp8_last_error() (per host thread).
