@@ -13,7 +13,8 @@ import os
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpa_fp8.so")
+# PA_FP8_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PA_FP8_LIB") or os.path.join(PKG, "libpa_fp8.so")
 
 PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
 

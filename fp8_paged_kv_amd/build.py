@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 
@@ -9,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa_fp8.so")
-SOURCES = ["pa_fp8_decode.hip", "pa_fp8_api.hip"]
+SOURCES = ["pa_fp8_decode.hip", "pa_fp8_decode_rows.hip", "pa_fp8_api.hip"]
 
 
 def hipcc() -> str:
@@ -19,21 +20,59 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
+# Per-source extra flags.  The whole-row kernels unroll a whole tile so that its
+# scores stay in statically indexed registers; LLVM's default size cap for
+# "#pragma unroll" would stop that.
+EXTRA = {"pa_fp8_decode_rows.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+
+
 def build(verbose: bool = False) -> str:
     """Always recompiles; writes fp8_paged_kv_amd/libpa_fp8.so."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # packed FP32 instructions stay off (ordinary scalar float code only)
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    base = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+            # packed FP32 instructions stay off (ordinary scalar float code only)
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Rpass-analysis=kernel-resource-usage",
+            "-I", os.path.join(ROOT, "include")]
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = base + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    remarks = []
+    for src, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n" + out + err)
+        remarks.append(err)
+    spills = scratch_kernels("\n".join(remarks))
+    if spills:
+        print("warning: kernels using scratch (register spills): " + ", ".join(spills))
     if verbose:
-        print(r.stderr)
+        print("\n".join(remarks))
+    tmp = LIB + ".tmp"
+    r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
     return LIB
+
+
+def scratch_kernels(remarks: str) -> list:
+    """Names of kernels whose resource-usage remark reports a nonzero ScratchSize."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            out.append(f"{name} ({m.group(1)} B/lane)")
+    return out
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 
 #include "../../include/pa_fp8.h"
 #include "pa_fp8_common.h"
@@ -71,15 +72,45 @@ int plan_splits(int B, int nkv, int max_tiles, int requested) {
 
 int rows_pad(int s1, int nq, int nkv) { return (s1 * (nq / nkv) + 15) / 16 * 16; }
 
+// CUs of the current device, queried once per device (the only state the library keeps).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// The whole-row path (one workgroup per CU, stream-K over (batch, tile, head))
+// serves the shapes it was built for when the caller leaves the split count to
+// the library; an explicit split count selects the per-head path.
+bool use_rows_path(int B, int s1, int nq, int nkv, int s2_tile, int num_splits) {
+    return num_splits == 0 && pa::rows_path_supported(nkv, s2_tile, s1 * (nq / nkv), s1, nq, B);
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
     size_t counters, part_ml, part_o, total;
 };
 
-// [B*nkv int32 counters | pad][B*nkv*nsplit*R*2 floats | pad][B*nkv*nsplit*R*128 floats]
-WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit) {
+// Per-head path with splits: [B*nkv int32 counters | pad][B*nkv*nsplit*R*2 | pad][B*nkv*nsplit*R*128]
+// Whole-row path:             [B*nkv+2 int32 partition| pad][B*nkv*KMAX*R*2 | pad][B*nkv*KMAX*R*128]
+// with KMAX = tiles per sequence at full capacity (a (batch, head) is split at most that often).
+WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit, bool rows, int kmax) {
     WorkspaceLayout l = {0, 0, 0, 0};
+    if (rows) {
+        const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
+        l.counters = 0;
+        l.part_ml = align256(((size_t)B * nkv + 2) * sizeof(int32_t));
+        l.part_o = l.part_ml + align256(units * kmax * R * 2 * sizeof(float));
+        l.total = l.part_o + units * kmax * R * pa::kHeadDim * sizeof(float);
+        return l;
+    }
     if (nsplit <= 1) return l;
     const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
     l.counters = 0;
@@ -108,9 +139,10 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
 
     const int capacity = max_blocks * block_size;
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
-    const int nsplit = plan_splits(B, nkv, max_tiles, num_splits);
+    const bool rows = use_rows_path(B, s1, nq, nkv, s2_tile, num_splits);
+    const int nsplit = rows ? 1 : plan_splits(B, nkv, max_tiles, num_splits);
     const int tps = (max_tiles + nsplit - 1) / nsplit;
-    const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit);
+    const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit, rows, max_tiles);
     const size_t need = lay.total;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)", need, nsplit,
@@ -132,10 +164,14 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.out = static_cast<uint16_t*>(out);
     if (need > 0) {
         char* base = static_cast<char*>(workspace);
-        p.counters = reinterpret_cast<int32_t*>(base + lay.counters);
+        if (rows)
+            p.rows_meta = reinterpret_cast<int32_t*>(base + lay.counters);
+        else
+            p.counters = reinterpret_cast<int32_t*>(base + lay.counters);
         p.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
         p.part_o = reinterpret_cast<float*>(base + lay.part_o);
     }
+    p.rows_kmax = max_tiles;
     p.dbg_rows = debug ? rows_dev : nullptr;
     p.dbg_q8 = debug ? q8_dev : nullptr;
     p.B = B;
@@ -153,7 +189,16 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.tiles_per_split = tps;
     p.softmax_scale = softmax_scale;
 
-    const hipError_t e = pa::launch_decode(p, static_cast<hipStream_t>(stream), debug);
+    hipError_t e;
+    if (rows) {
+        if (debug && p.dbg_rows) {
+            e = pa::launch_fill_rows(p, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+        }
+        e = pa::launch_decode_rows(p, device_cus(), static_cast<hipStream_t>(stream), debug);
+    } else {
+        e = pa::launch_decode(p, static_cast<hipStream_t>(stream), debug);
+    }
     if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
     return PA_OK;
 }
@@ -171,8 +216,9 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
     if (st != PA_OK) return st;
     const int capacity = max_blocks_per_seq * block_size;
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
-    const int nsplit = plan_splits(B, nkv, max_tiles, num_splits);
-    *bytes_host = layout_for(B, s1, nq, nkv, nsplit).total;
+    const bool rows = use_rows_path(B, s1, nq, nkv, s2_tile, num_splits);
+    const int nsplit = rows ? 1 : plan_splits(B, nkv, max_tiles, num_splits);
+    *bytes_host = layout_for(B, s1, nq, nkv, nsplit, rows, max_tiles).total;
     if (splits_host) *splits_host = nsplit;
     return PA_OK;
 }

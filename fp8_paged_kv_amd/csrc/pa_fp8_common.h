@@ -23,15 +23,20 @@ struct DecodeParams {
     int32_t* counters;          // [B*nkv] arrival counters (zero between calls)  (nsplit > 1)
     float* part_o;              // [B*nkv, nsplit, rows_pad, 128]
     float* part_ml;             // [B*nkv, nsplit, rows_pad, 2]  (M in log2 units, L)
+    int32_t* rows_meta;         // whole-row path: tile prefix over (batch, head group), U, workgroups used
     int32_t* dbg_rows;          // [B, capacity] or null
     uint8_t* dbg_q8;            // [B*s1, nq, 128] or null
     int B, s1, nq, nkv, G, rows;
     int s2_tile, max_blocks, num_blocks, capacity;
     int nsplit, nsplit_pad, tiles_per_split;
+    int rows_kmax;              // whole-row path: partial slots per (batch, KV head)
     float softmax_scale;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, bool debug);
 int grid_size(const DecodeParams& p);
+bool rows_path_supported(int nkv, int s2_tile, int rows, int s1, int nq, int B);
+hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t stream, bool debug);
+hipError_t launch_fill_rows(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace pa

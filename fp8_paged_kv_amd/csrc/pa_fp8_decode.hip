@@ -43,92 +43,9 @@
 #include <stdint.h>
 
 #include "pa_fp8_common.h"
+#include "pa_fp8_device.h"
 
 namespace pa {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLog2_448 = 8.807354922057604f;   // log2(448)
-
-// ---------------------------------------------------------------- helpers
-
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// 4x4 byte transpose: out[c] byte k = in[k] byte c.
-__device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                           uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
-    const uint32_t e0 = perm(b, a, 0x06020400u);   // a0 b0 a2 b2
-    const uint32_t e1 = perm(b, a, 0x07030501u);   // a1 b1 a3 b3
-    const uint32_t f0 = perm(d, c, 0x06020400u);   // c0 d0 c2 d2
-    const uint32_t f1 = perm(d, c, 0x07030501u);   // c1 d1 c3 d3
-    o0 = perm(f0, e0, 0x05040100u);                // a0 b0 c0 d0
-    o1 = perm(f1, e1, 0x05040100u);                // a1 b1 c1 d1
-    o2 = perm(f0, e0, 0x07060302u);                // a2 b2 c2 d2
-    o3 = perm(f1, e1, 0x07060302u);                // a3 b3 c3 d3
-}
-
-// Four FP32 values to four E4M3 codes (RNE, no clamp), byte i = value i.
-__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
-// Four E4M3 codes (bytes of w) -> four exact bf16 values in two dwords.
-__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    lo = __builtin_bit_cast(uint32_t, a);
-    hi = __builtin_bit_cast(uint32_t, b);
-}
-
-// Eight E4M3 codes (two dwords) -> the bf16x8 operand of one MFMA.
-__device__ __forceinline__ bf16x8 fp8x8_to_op(uint32_t w0, uint32_t w1) {
-    uint32_t d0, d1, d2, d3;
-    fp8x4_to_bf16(w0, d0, d1);
-    fp8x4_to_bf16(w1, d2, d3);
-    const i32x4 v = {(int)d0, (int)d1, (int)d2, (int)d3};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-    return __uint_as_float(((uint32_t)h) << 16);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// Broadcast lane n of every 16-lane row to the whole row (DPP row_newbcast).
-template <int N>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ float wave_max_over_groups(float v) {
-    // max over lanes {l, l^16, l^32, l^48}
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum_over_groups(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
 
 // Workgroup placement.  Workgroups are dealt round-robin over the 8 XCDs
 // (id x runs on XCD x % 8), each XCD with its own L2.  A work unit is a
@@ -160,18 +77,11 @@ __device__ __forceinline__ Placement place(int x, int B, int nsplit, int nsplit_
     return r;
 }
 
-// token of k-slot (lane group g, byte j) inside a 32-token chunk; equals the
-// token held in element i of MFMA block k of the S^T accumulator (j = 4k + i)
-__device__ __forceinline__ int chunk_token(int g, int j) {
-    return (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4);
-}
-
 // ------------------------------------------------------------------ kernel
 
 // ------------------------------------------------------------------ kernel
 
 constexpr int kRing = 4;                  // register ring of chunk buffers (3 in flight)
-constexpr float kDropLog2 = 40.f;         // tiles 2^40 below the running max are dropped
 
 // One prefetched chunk: 16 dwords of K (two 16-token blocks x 32 bytes) or of
 // V (8 tokens x 8 bytes), plus the lane's k_scale word for K chunks.
@@ -245,24 +155,9 @@ void decode_kernel(DecodeParams a) {
                 const int d0 = half * 64 + 16 * lg;
                 const i32x4 v0 = *reinterpret_cast<const i32x4*>(qp + d0);
                 const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + d0 + 8);
-                uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
-                                   (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
-                float x[16];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    x[2 * i] = bf16_to_f32((uint16_t)(raw[i] & 0xffffu));
-                    x[2 * i + 1] = bf16_to_f32((uint16_t)(raw[i] >> 16));
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    // IEEE divide (the codes are decided in FP32), then saturate:
-                    // the gfx950 convert rounds to nearest even but does not clamp.
-                    const float y = (qs == 0.f) ? 0.f : x[i] / qs;
-                    x[i] = __builtin_amdgcn_fmed3f(y, -448.f, 448.f);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    wds[half * 4 + i] = cvt4_fp8(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+                const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
+                                         (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
+                quantise_q16(raw, qs, &wds[half * 4]);
             }
             if (DBG && sp == 0 && w == 0 && a.dbg_q8) {
                 uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;
@@ -639,6 +534,13 @@ static hipError_t launch_tile(const DecodeParams& p, int nrb, int grid, hipStrea
         case 3: return launch_nrb<3, NW, CPW>(p, grid, st, dbg);
         default: return launch_nrb<4, NW, CPW>(p, grid, st, dbg);
     }
+}
+
+hipError_t launch_fill_rows(const DecodeParams& p, hipStream_t st) {
+    const int64_t n = (int64_t)p.B * p.capacity;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256),
+                       0, st, p.dbg_rows, n, -1);
+    return hipGetLastError();
 }
 
 int grid_size(const DecodeParams& p) {
