@@ -20,16 +20,16 @@ struct DecodeParams {
     const int32_t* block_table; // [B, max_blocks]
     const int32_t* seqs;        // [B]
     uint16_t* out;              // [B*s1, nq, 128] bf16
-    int32_t* counters;          // [B*nkv] arrival counters (zero between calls)  (nsplit > 1)
+    int32_t* counters;          // per-head path: [B*nkv] arrival counters (zero between calls)
+    int32_t* rows_meta;         // whole-row path: cost prefix over (batch, head group), workgroups used
     float* part_o;              // [B*nkv, nsplit, rows_pad, 128]
     float* part_ml;             // [B*nkv, nsplit, rows_pad, 2]  (M in log2 units, L)
-    int32_t* rows_meta;         // whole-row path: tile prefix over (batch, head group), U, workgroups used
     int32_t* dbg_rows;          // [B, capacity] or null
     uint8_t* dbg_q8;            // [B*s1, nq, 128] or null
     int B, s1, nq, nkv, G, rows;
     int s2_tile, max_blocks, num_blocks, capacity;
     int nsplit, nsplit_pad, tiles_per_split;
-    int rows_kmax;              // whole-row path: partial slots per (batch, KV head)
+    int rows_kmax;              // whole-row path: partial slots per (batch, KV head) = tiles
     float softmax_scale;
 };
 

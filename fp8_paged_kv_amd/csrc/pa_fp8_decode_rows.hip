@@ -2,28 +2,28 @@
 //
 // Same operation as the per-head path (web page "PyPTO 实现 GLM-4.5 Paged
 // Attention FP8 量化算子…", section 计算流程 steps 1-10), organised for the
-// memory system:
+// memory system and for one wave per SIMD:
 //
-//  * One workgroup holds one wave per KV head (nkv <= 8) and reads whole
-//    token rows of the cache ([token][all KV heads][128] bytes, contiguous)
-//    with gfx950's direct global->LDS loads.  Every wave then takes its own
-//    head's bytes from LDS.  Reading whole rows keeps DRAM pages fully used;
-//    one workgroup per head reading 128 of every 1024 bytes measured ~17 %
-//    slower on this pattern.
-//  * The LDS ring holds NST stages of one 32-token chunk (K or V of all
-//    heads, plus k_scale); loads for the next NST-1 chunks are always in
-//    flight and cost no registers.  LDS-DMA completion is not tracked by the
-//    compiler, so every step waits with an explicit vmcnt and a raw barrier.
-//  * Work is balanced "stream-K" style: the (batch, tile, head) atoms of the
-//    whole call, in that order, are split into equal contiguous ranges, one
-//    per workgroup (one workgroup per CU).  A range may cover parts of
-//    several sequences and only some heads of its first and last tile.  A
-//    (batch, head) handled by one workgroup is finished in place; otherwise
-//    each workgroup writes an (O, M, L) partial and a second small kernel
-//    merges them in range order.
-//  * Each wave keeps the whole tile's scores S (s2_tile x 16 rows, fp32) in
-//    registers, since the FP8 quantisation of P needs the tile's row max
-//    before any P of the tile is used.
+//  * A workgroup serves a group of HG <= 2 KV heads with 2*HG waves: wave
+//    w = 2*hl + p owns head hl of the group and token half p of every
+//    128-token cache block.  The two waves of a head exchange their row
+//    maxima through LDS at the end of a tile's K pass, so both quantise P with
+//    the maximum of the whole tile, exactly as one wave holding the tile would;
+//    each then keeps only half of the tile's scores in registers.
+//  * A step stages one cache block (128 tokens x the group's 128-byte head
+//    slices, contiguous per token row) through an LDS ring filled by direct
+//    global->LDS loads with a scalar base and 32-bit lane offsets.  Two steps
+//    are always in flight.  The loads are issued from inline asm so the
+//    compiler does not see them as LDS stores (it would otherwise drain them
+//    before every LDS read); completion is ordered by hand with an explicit
+//    vmcnt wait and a raw barrier at every step.
+//  * Work unit = one tile of one (batch, head group).  The units of the whole
+//    call, in (batch, group, tile) order, are split into contiguous ranges of
+//    equal cost (steps = 2 x valid blocks), one per workgroup; blocks past a
+//    sequence's end cost nothing and are not visited.  A (batch, group) whose
+//    tiles land in one workgroup is finished in place.  Otherwise every
+//    workgroup writes an (O, M, L) partial and a second, small kernel merges
+//    them (the kernel boundary orders the writes; no fences or atomics).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,305 +34,342 @@ namespace pa {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Direct global->LDS loads (lane i writes dst + size * i), issued from inline
-// asm so that the compiler does not see them as LDS stores.  Otherwise it
-// conservatively waits for every load in flight (vmcnt(0)) before any LDS read
-// of the ring, which would serialise the prefetch.  Their completion is
-// ordered by hand with wait_vm<N>() and a barrier.
+// A wave-uniform pointer, forced into scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global->LDS loads: lane i writes dst + size * i from sbase + voff_i.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_b128(const void* src, lds_ptr dst) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"((uint32_t)(uintptr_t)dst) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, lds_ptr dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(uniform_ptr(sbase)), "s"((uint32_t)(uintptr_t)dst) : "memory", "m0");
 }
-__device__ __forceinline__ void dma_b32(const void* src, lds_ptr dst) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(src), "s"((uint32_t)(uintptr_t)dst) : "memory", "m0");
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, lds_ptr dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(uniform_ptr(sbase)), "s"((uint32_t)(uintptr_t)dst) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
-// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt left free), gfx9 encoding.  vmcnt counts
-// this wave's vector memory operations, which complete in issue order.
+// s_waitcnt vmcnt(N) lgkmcnt(0), gfx9 encoding.  vmcnt counts this wave's
+// vector memory operations, which complete in issue order.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0) only (vmcnt left at its maximum, 63).
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 // Workgroup barrier that is also a compiler memory barrier, without the
-// release fence of __syncthreads (which would wait for every DMA in flight).
+// release fence of __syncthreads (which would wait for every load in flight).
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
 // Load of a wave-uniform int32 through the constant address space, i.e. as a
-// scalar load.  A vector load would share the in-order vmcnt counter with the
-// ring's loads, and waiting for its result would drain the whole ring.
+// scalar load (a vector load would share vmcnt with the ring's loads).
 __device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-// Swizzle of 16-byte slots inside a staged chunk: slot (token t, piece p) is
-// stored at t * 8HG + (p ^ f(t)).  K reads (16 tokens, one piece) and V
-// reads (tokens t and t+4, eight pieces) then hit distinct LDS banks.
-template <int HG>
-__device__ __forceinline__ int swz(int t) {
-    if (HG == 1) return (t >> 1) & 7;
-    return (t & 15) ^ ((t & 4) << 1);
-}
+__device__ __forceinline__ int lds_uniform(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
 
-// One unit = one tile of one virtual sequence (batch b, heads h0 .. h0+HG-1);
-// the workgroup works on heads [hlo, hhi) of the group in it.
-struct RowsUnit {
-    int v, b, h0, t, hlo, hhi, seq;
-};
+constexpr int kStepTok = 128;             // tokens per step = one cache block
+constexpr int kPrefixMax = 1024;          // (batch, head group) pairs of one call
 
-constexpr int kQRowsMax = 128;            // s1 * nq rows of one sequence staged in LDS
-constexpr int kPrefixMax = 1024;          // batch size limit of this path
-
-template <int NRB, int NCH, int HG, int NST, bool DBG>
-__global__ __launch_bounds__(HG * 64) void decode_rows_kernel(DecodeParams a) {
-    constexpr int T = NCH * 32;           // s2_tile
-    constexpr int R = NRB * 16;
-    constexpr int CHUNK = HG * 4096;      // bytes of one staged chunk (32 tokens, HG heads)
-    constexpr int STEPS = 2 * NCH;        // per unit: NCH chunks of K, then NCH of V
-    constexpr int AHEAD = NST - 1;        // chunks in flight
-    constexpr int PER_STEP = 5;           // loads per wave and step: 4 chunk + 1 k_scale
-    constexpr int TOK16 = 16 * 8 * HG * 16;   // LDS bytes of 16 staged tokens
-    static_assert(AHEAD >= 1 && AHEAD < STEPS, "ring depth");
-    // Per virtual sequence: Q rows of the batch (1 KB loads), q_scale (dword loads)
-    // and v_scale of the group's heads (1 KB loads).  Every wave issues exactly QNW of
-    // them (padded with loads of a hot line) so the wait counts are static.
-    constexpr int QI = kQRowsMax * 256 / 1024, QSI = kQRowsMax / 64, VSI = (HG * kHeadDim * 4 + 1023) / 1024;
-    constexpr int QNW = (QI + QSI + VSI + HG - 1) / HG;
+template <int NRB, int NBLK, int HG, bool DBG>
+__global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a) {
+    constexpr int NW = 2 * HG;            // waves: w = 2 * hl + p
+    constexpr int NST = 3, AHEAD = 2;     // ring stages, steps in flight
+    constexpr int T = NBLK * kStepTok;    // s2_tile
+    constexpr int R = NRB * 16;           // padded query rows per head
+    constexpr int NPC = 8 * HG;           // 16-byte pieces of a staged token (the group's heads)
+    constexpr int TOKB = NPC * 16;        // LDS bytes of a staged token
+    constexpr int STEP_BYTES = kStepTok * TOKB;
+    constexpr int DPW = STEP_BYTES / 1024 / NW;   // 1 KB loads per wave and step
+    constexpr int PER_STEP = DPW + 1;     // + the k_scale load
+    constexpr int NQ = 2 * NBLK;          // 32-token chunks of a tile held by one wave
+    constexpr int QROWS = 32 * HG;        // staged query rows (HG heads x <= 32 rows)
+    constexpr int QI = QROWS * 256 / 1024, QNW = (QI + 2 + NW - 1) / NW;
+    static_assert(DPW == 8, "eight 1 KB loads per wave and step");
     static_assert(PER_STEP * (AHEAD - 1) + QNW < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring[NST][CHUNK];
-    __shared__ __attribute__((aligned(16))) float s_ks[NST][HG][64];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[kQRowsMax * 256];
-    __shared__ __attribute__((aligned(16))) float s_qs[kQRowsMax];
-    __shared__ int s_pref[kPrefixMax + 1];
-    // v_scale of the group's heads, double-buffered: the next sequence's is staged
-    // before the current one's flush has read it.  Rows padded to whole 1 KB loads.
-    __shared__ __attribute__((aligned(16))) float s_vs[2][VSI * 2][kHeadDim];
-    __shared__ __attribute__((aligned(16))) float s_qpad[HG][64];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring[NST][STEP_BYTES];
+    __shared__ __attribute__((aligned(16))) float s_ks[NST][NW][64];
+    // query rows, q_scale and v_scale of the group, double-buffered by segment parity: the
+    // next sequence's are staged while the current one may still be reading its own
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[2][QROWS * 256];
+    __shared__ __attribute__((aligned(16))) float s_qs[2][64];
+    __shared__ __attribute__((aligned(16))) float s_vs[2][256];
+    __shared__ __attribute__((aligned(16))) float s_comb[HG][16 * kHeadDim + 16];
+    __shared__ __attribute__((aligned(16))) float s_max[NW][R];
+    __shared__ __attribute__((aligned(16))) float s_qpad[NW][64];
+    __shared__ int s_pref[kPrefixMax + 1];   // exclusive cost prefix over (batch, group), in steps
+    __shared__ int s_seq[kPrefixMax];        // clamped length per batch
+    __shared__ int s_units;
 
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // head of the group
-    const int lr = lane & 15;
-    const int lg = lane >> 4;
-    const int NG = a.nkv / HG;            // head groups per token row
-    const int BV = a.B * NG;              // virtual sequences: (batch, head group)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = w >> 1, p = w & 1;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int B = a.B, NG = a.nkv / HG, BV = B * NG;
+    const int nkv = a.nkv;
 
-    // ---- tiles per virtual sequence and their exclusive prefix (wave 0) -------------------
+    // ---- lengths, cost prefix and unit count ------------------------------------------------
+    for (int b = threadIdx.x; b < B; b += NW * 64) {
+        const int s = a.seqs[b];
+        s_seq[b] = s < 0 ? 0 : (s > a.capacity ? a.capacity : s);
+    }
+    __syncthreads();
     if (w == 0) {
         const int strip = (BV + 63) / 64;
         const int v0 = lane * strip, v1 = min(v0 + strip, BV);
-        int sum = 0;
+        int cost = 0, units = 0;
         for (int v = v0; v < v1; ++v) {
-            int s = a.seqs[v / NG];
-            s = s < 0 ? 0 : (s > a.capacity ? a.capacity : s);
-            sum += (s + T - 1) / T;
+            const int s = s_seq[v / NG];
+            cost += 2 * ((s + kStepTok - 1) / kStepTok);
+            units += (s + T - 1) / T;
         }
-        int incl = sum;
+        int incl = cost;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int x = __shfl_up(incl, o, 64);
             if (lane >= o) incl += x;
         }
-        int run = incl - sum;
+        int run = incl - cost;
         for (int v = v0; v < v1; ++v) {
             s_pref[v] = run;
-            int s = a.seqs[v / NG];
-            s = s < 0 ? 0 : (s > a.capacity ? a.capacity : s);
-            run += (s + T - 1) / T;
+            run += 2 * ((s_seq[v / NG] + kStepTok - 1) / kStepTok);
         }
         if (lane == 63) s_pref[BV] = incl;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) units += __shfl_xor(units, o, 64);
+        if (lane == 0) s_units = units;
     }
     __syncthreads();
-    const int U = __builtin_amdgcn_readfirstlane(s_pref[BV]);
+    const int64_t C = lds_uniform(&s_pref[BV]);
+    const int U = lds_uniform(&s_units);
     const int Geff = min((int)gridDim.x, U);
     const int g = blockIdx.x;
 
     if (g == 0) {
-        // publish the partition for the merge kernel; zero the rows of empty sequences
-        for (int i = threadIdx.x; i <= BV; i += HG * 64) a.rows_meta[i] = s_pref[i];
+        // the partition, for the merge kernel: cost prefix over (batch, group), then Geff
+        for (int i = threadIdx.x; i <= BV; i += NW * 64) a.rows_meta[i] = s_pref[i];
         if (threadIdx.x == 0) a.rows_meta[BV + 1] = Geff;
-        for (int b = 0; b < a.B; ++b) {
-            if (s_pref[b * NG + NG] != s_pref[b * NG]) continue;
-            for (int e = threadIdx.x; e < a.s1 * a.nq * kHeadDim; e += HG * 64)
+        // rows of empty sequences are zero
+        for (int b = 0; b < B; ++b) {
+            if (s_seq[b] != 0) continue;
+            for (int e = threadIdx.x; e < a.s1 * a.nq * kHeadDim; e += NW * 64)
                 a.out[(int64_t)b * a.s1 * a.nq * kHeadDim + e] = 0;
         }
     }
     if (g >= Geff) return;
 
-    // Atoms (tile u, head w of the group) are numbered u * HG + w; this workgroup
-    // owns [a0, a1).  Every range holds at least HG atoms (Geff <= U), so it
-    // meets every head of the group.
-    const int64_t A = (int64_t)U * HG;
-    const int64_t a0 = (int64_t)g * A / Geff, a1 = (int64_t)(g + 1) * A / Geff;
-    const int u_first = (int)(a0 / HG), u_end = (int)((a1 - 1) / HG) + 1;
-
-    auto unit_info = [&](int u) -> RowsUnit {
-        RowsUnit r;
-        int lo = 0, hi = BV - 1;              // largest v with s_pref[v] <= u
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (__builtin_amdgcn_readfirstlane(s_pref[mid]) <= u) lo = mid; else hi = mid - 1;
-        }
-        r.v = lo;                             // s_pref[lo] <= u < s_pref[lo + 1]
-        r.b = lo / NG;
-        r.h0 = (lo - r.b * NG) * HG;
-        r.t = u - __builtin_amdgcn_readfirstlane(s_pref[lo]);
-        r.hlo = (int)max((int64_t)0, a0 - (int64_t)u * HG);
-        r.hhi = (int)min((int64_t)HG, a1 - (int64_t)u * HG);
-        const int s = ld_uniform(a.seqs, r.b);
-        r.seq = s < 0 ? 0 : (s > a.capacity ? a.capacity : s);
-        return r;
+    // Unit (v, t) spans cost [s_pref[v] + 2 NBLK t, + 2 nvs); its midpoint mid(v, t)
+    // decides its workgroup: workgroup g owns the units whose midpoints lie in [lo, hi),
+    // so a range is off its share by at most half a unit.  owner(x) is the workgroup
+    // whose range holds x.
+    const int64_t lo = (int64_t)g * C / Geff, hi = (int64_t)(g + 1) * C / Geff;
+    auto seq_of = [&](int v) { return lds_uniform(&s_seq[v / NG]); };
+    auto ntiles = [&](int v) { return (seq_of(v) + T - 1) / T; };
+    auto mid_of = [&](int v, int t) -> int64_t {
+        const int nb = (seq_of(v) + kStepTok - 1) / kStepTok;
+        return lds_uniform(&s_pref[v]) + 2LL * NBLK * t + min(NBLK, nb - t * NBLK);
+    };
+    auto owner = [&](int64_t x) -> int { return (int)(((x + 1) * Geff - 1) / C); };
+    // first tile t of non-empty v with mid(v, t) >= x (ntiles(v) if none)
+    auto first_tile_from = [&](int v, int64_t x) -> int {
+        const int nt = ntiles(v);
+        const int64_t d = x - lds_uniform(&s_pref[v]) - NBLK;          // mid of a full tile t: pv + NBLK (2t + 1)
+        int t = d <= 0 ? 0 : (int)min((int64_t)nt, (d + 2 * NBLK - 1) / (2 * NBLK));
+        while (t > 0 && mid_of(v, t - 1) >= x) --t;                  // the last tile's midpoint is earlier
+        while (t < nt && mid_of(v, t) < x) ++t;
+        return t;
+    };
+    auto next_nonempty = [&](int v) {
+        while (v < BV && ntiles(v) == 0) ++v;
+        return v;
     };
 
-    // ---- per-lane constants of the staged layout ----------------------------------------
-    const int64_t tok_stride = (int64_t)a.nkv * kHeadDim;      // one token row, all heads
-    // DMA: load i of wave w fills 16-byte slots [(4w + i) 64, +64); slot -> (token, piece)
-    uint32_t dmaoff[4];
+    struct Unit {
+        int v, b, h0, t, seq, nvs;        // nvs = valid blocks (steps per pass); 0 = no unit
+        int ids;                          // lane i < NBLK: physical block of block i of the tile
+    };
+    auto make_unit = [&](int v, int t, bool ok) -> Unit {
+        Unit u;
+        u.v = v;
+        u.b = ok ? v / NG : 0;
+        u.h0 = ok ? (v - u.b * NG) * HG : 0;
+        u.t = t;
+        u.seq = ok ? seq_of(v) : 0;
+        u.nvs = ok ? min(NBLK, (u.seq + kStepTok - 1) / kStepTok - t * NBLK) : 0;
+        // block ids live in one VGPR (lane i = block i) to keep scalar registers free
+        int raw[NBLK];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s = (4 * w + i) * 64 + lane;
-        const int t = s / (8 * HG);
-        const int p = (s % (8 * HG)) ^ swz<HG>(t);
-        dmaoff[i] = (uint32_t)(t * tok_stride + 16 * p);
+        for (int i = 0; i < NBLK; ++i)
+            raw[i] = ok ? ld_uniform(a.block_table, (int64_t)u.b * a.max_blocks + min(t * NBLK + i, a.max_blocks - 1)) : 0;
+        u.ids = 0;
+#pragma unroll
+        for (int i = 0; i < NBLK; ++i)
+            u.ids = (lane == i) ? ((i < u.nvs && raw[i] >= 0 && raw[i] < a.num_blocks) ? raw[i] : 0) : u.ids;
+        return u;
+    };
+    // the unit after (v, t) in this workgroup's range, or none
+    auto next_unit = [&](const Unit& u) -> Unit {
+        int v = u.v, t = u.t + 1;
+        if (t >= ntiles(v)) {
+            v = next_nonempty(v + 1);
+            t = 0;
+        }
+        const bool ok = v < BV && mid_of(v, t) < hi;
+        return make_unit(ok ? v : 0, t, ok);
+    };
+
+    // first unit: the first midpoint >= lo
+    Unit cur;
+    {
+        int vlo = 0, vhi = BV - 1;            // largest v with s_pref[v] <= lo
+        while (vlo < vhi) {
+            const int mid = (vlo + vhi + 1) >> 1;
+            if (lds_uniform(&s_pref[mid]) <= lo) vlo = mid; else vhi = mid - 1;
+        }
+        int v = next_nonempty(vlo), t = 0;
+        if (v < BV) {
+            t = first_tile_from(v, lo);
+            if (t >= ntiles(v)) {
+                v = next_nonempty(v + 1);
+                t = 0;
+            }
+        }
+        if (v >= BV || mid_of(v, t) >= hi) return;   // no midpoint in this range: no work
+        cur = make_unit(v, t, true);
     }
-    // K operand reads: token lr (+16), pieces 8w + lg and 8w + 4 + lg.  V operand
-    // reads: token chunk_token(lg, j), bytes [8lr, 8lr + 8) of head w.  Token t + 16
-    // has the swizzle of t, so the second half is a constant offset.
+    Unit nxt = next_unit(cur);
+
+    // ---- per-lane constants of the staged layout ----------------------------------------------
+    // Slot (token t, physical piece pp) holds logical piece pp ^ (t mod NPC) of token t.
+    const int64_t tok_stride = (int64_t)nkv * kHeadDim;        // bytes of one token row (all heads)
+    uint32_t dmaoff[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+        const int s = (DPW * w + i) * 64 + lane;
+        const int t = s / NPC, pp = s % NPC;
+        dmaoff[i] = (uint32_t)(t * tok_stride + 16 * (pp ^ (t & (NPC - 1))));
+    }
+    // K operand (token 16k + lr of a chunk; pieces 8hl + lg and 8hl + 4 + lg) and V operand
+    // (token chunk_token(lg, j); bytes 8lr .. 8lr + 7 of head hl).  Tokens that differ by a
+    // multiple of 16 share a swizzle, so chunk and half offsets are constants.
     int kslot[2], vaddr[4];
 #pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-        const int t = lr, p = 8 * w + 4 * hlf + lg;
-        kslot[hlf] = (t * 8 * HG + (p ^ swz<HG>(t))) * 16;
-    }
+    for (int hlf = 0; hlf < 2; ++hlf)
+        kslot[hlf] = (lr * NPC + ((8 * hl + 4 * hlf + lg) ^ (lr & (NPC - 1)))) * 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int t = chunk_token(lg, j), p = 8 * w + (lr >> 1);
-        vaddr[j] = (t * 8 * HG + (p ^ swz<HG>(t))) * 16 + 8 * (lr & 1);
+        const int t = chunk_token(lg, j), pc = 8 * hl + (lr >> 1);
+        vaddr[j] = (t * NPC + (pc ^ (t & (NPC - 1)))) * 16 + 8 * (lr & 1);
     }
+    const uint32_t ksoff = (uint32_t)(lane * nkv * 4);
 
-    const int qrows_ = a.s1 * a.nq;
-    const int qbytes_ = qrows_ * 256;
-    const int lane_ = lane;
-
-    // Physical first token row of each 128-token block of a unit's tile (scalar).
-    constexpr int BPT = T / kBlock;
-    struct UnitBlocks {
-        int64_t row0[BPT];
-    };
-    auto unit_blocks = [&](const RowsUnit& ui, bool ok) -> UnitBlocks {
-        UnitBlocks ub;
-        // all entries are loaded (index clamped to the row) so the loads issue together
-        int raw[BPT];
+    // Issue the loads of step `idx` of unit u (K pass: idx < nvs, then the V pass) into
+    // stage st: DPW block loads and one k_scale load per wave, always PER_STEP.  A step
+    // past the last unit (nvs == 0) reloads block 0.
+    auto issue = [&](const Unit& u, int idx, int st) {
+        const bool ok = u.nvs > 0;
+        const bool isv = ok && idx >= u.nvs;
+        const int blk = isv ? idx - u.nvs : (ok ? idx : 0);
+        const int id = __builtin_amdgcn_readlane(u.ids, blk);
+        const int64_t row0 = (int64_t)id * kStepTok;
+        const uint8_t* base = (isv ? a.v_cache : a.k_cache) + row0 * tok_stride + u.h0 * kHeadDim;
 #pragma unroll
-        for (int i = 0; i < BPT; ++i)
-            raw[i] = ld_uniform(a.block_table, (int64_t)ui.b * a.max_blocks + min(ui.t * BPT + i, a.max_blocks - 1));
-#pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int p = ui.t * T + i * kBlock;
-            const int id = (ok && p < ui.seq && raw[i] >= 0 && raw[i] < a.num_blocks) ? raw[i] : 0;
-            ub.row0[i] = (int64_t)id * kBlock;
-        }
-        return ub;
+        for (int i = 0; i < DPW; ++i) dma16(base, dmaoff[i], (lds_ptr)(&s_ring[st][(DPW * w + i) * 1024]));
+        // k_scale of head h0 + hl, tokens 64p + lane of the block
+        const float* ksb = a.k_scale + (row0 + 64 * p) * nkv + u.h0 + hl;
+        dma4(ksb, ksoff, (lds_ptr)(&s_ks[st][w][0]));
     };
 
-    // Issue the loads of step `r` (static) of a unit into ring stage `st`:
-    // 4 chunk loads and one k_scale load per wave (PER_STEP, always).
-    auto issue = [&](int r, int st, const RowsUnit& ui, const UnitBlocks& ub, bool unit_ok) {
-        const int c = r < NCH ? r : r - NCH;
-        const bool isv = r >= NCH;
-        const bool valid = unit_ok && ui.t * T + 32 * c < ui.seq;
-        const bool full = ui.hlo == 0 && ui.hhi == HG;
-        const int64_t slot0 = valid ? ub.row0[c / 4] + 32 * (c % 4) : 0;
-        const uint8_t* cache = isv ? a.v_cache : a.k_cache;
-        const uint8_t* base = cache + slot0 * tok_stride + ui.h0 * kHeadDim;
-        int ln = lane_;
-        asm volatile("" : "+v"(ln));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bool use = valid;
-            if (!full) {
-                // only the heads of this workgroup's atoms are read
-                const int s = (4 * w + i) * 64 + ln;
-                const int t = s / (8 * HG);
-                const int head = ((s % (8 * HG)) ^ swz<HG>(t)) >> 3;
-                use = use && head >= ui.hlo && head < ui.hhi;
-            }
-            const uint8_t* src = use ? base + dmaoff[i] : cache + 16 * ln;   // unused lanes: a hot line
-            dma_b128(src, (lds_ptr)(&s_ring[st][(4 * w + i) * 1024]));
-        }
-        // k_scale of head w, tokens lane & 31 (lanes 32-63 repeat them)
-        const bool kuse = valid && !isv && w >= ui.hlo && w < ui.hhi;
-        const float* ksrc = kuse ? a.k_scale + (slot0 + (ln & 31)) * a.nkv + ui.h0 + w : a.k_scale + (ln & 31);
-        dma_b32(ksrc, (lds_ptr)(&s_ks[st][w][0]));
-    };
-
-    // The QNW loads of this wave that stage Q and q_scale of batch b and v_scale of
-    // heads h0 .. h0+HG-1.  Rare (once per virtual sequence), so the addresses are
-    // recomputed on every call: the opaque copies keep the compiler from hoisting
-    // them out of the loop.
+    // The QNW loads of this wave that stage the query rows and q_scale of heads
+    // h0 .. h0+HG-1 of batch b (staged row hl * rows + rr) and their v_scale.
+    // Rare (once per sequence), so the lane values are recomputed on every call.
+    const int rows = a.rows;
     auto issue_q = [&](int b, int h0, int buf) {
-        int lane = lane_, qbytes = qbytes_, qrows = qrows_;
-        asm volatile("" : "+v"(lane));
-        asm volatile("" : "+s"(qbytes), "+s"(qrows));
-        const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q) + (int64_t)b * qbytes;
-        const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v_scale + ((int64_t)b * a.nkv + h0) * kHeadDim);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int qrow0 = b * a.s1 * a.nq;                     // first query row of batch b
+        auto src_row = [&](int sr) {                            // staged row -> query row
+            const int hs = sr / rows, rr = sr - hs * rows;
+            const int s = rr / a.G, gq = rr - s * a.G;
+            return qrow0 + s * a.nq + (h0 + hs) * a.G + gq;
+        };
 #pragma unroll
         for (int n = 0; n < QNW; ++n) {
-            const int j = w + n * HG;
+            const int j = w + n * NW;
             if (j < QI) {
-                const int off = j * 1024 + 16 * lane;
-                const uint8_t* src = off < qbytes ? qb + off : qb;        // past the rows: a line of them
-                dma_b128(src, (lds_ptr)(&s_q[j * 1024]));
-            } else if (j < QI + QSI) {
-                const int row = (j - QI) * 64 + lane;
-                const float* src = a.q_scale + (int64_t)b * qrows + (row < qrows ? row : 0);
-                dma_b32(src, (lds_ptr)(&s_qs[(j - QI) * 64]));
-            } else if (j < QI + QSI + VSI) {
-                const int off = (j - QI - QSI) * 1024 + 16 * lane;
-                const uint8_t* src = off < HG * kHeadDim * 4 ? vb + off : vb;
-                dma_b128(src, (lds_ptr)(reinterpret_cast<uint8_t*>(&s_vs[buf][0][0]) + (j - QI - QSI) * 1024));
+                const int sr = 4 * j + (ln >> 4);
+                const int row = sr < HG * rows ? src_row(sr) : qrow0;
+                dma16(a.q, (uint32_t)(row * 256 + 16 * (ln & 15)), (lds_ptr)(&s_q[buf][j * 1024]));
+            } else if (j == QI) {
+                const int row = ln < HG * rows ? src_row(ln) : qrow0;
+                dma4(a.q_scale, (uint32_t)(row * 4), (lds_ptr)(&s_qs[buf][0]));
+            } else if (j == QI + 1) {
+                const uint32_t vb = (uint32_t)((b * nkv + h0) * kHeadDim * 4);
+                dma16(a.v_scale, vb + (16 * ln < HG * kHeadDim * 4 ? 16 * ln : 0), (lds_ptr)(&s_vs[buf][0]));
             } else {
-                // padding: reload the batch's first q_scale into this wave's own slot
-                dma_b32(a.q_scale + (int64_t)b * qrows, (lds_ptr)(&s_qpad[w][0]));
+                dma4(a.q_scale, (uint32_t)(qrow0 * 4), (lds_ptr)(&s_qpad[w][0]));
             }
         }
     };
 
-    // ---- running state of this wave's head ------------------------------------------------
+    // ---- running state of this wave (head hl, token half p) -----------------------------------
     bf16x8 qop[NRB][4];
     float qcoef[NRB];
     float M_s[NRB], L_s[NRB], M_o[NRB][4];
     f32x4 O[NRB][8];
-    bool has_state = false;
+    int seg_t0 = 0;                          // first tile of the current segment
 
-    // prologue: Q of the first virtual sequence, then the first AHEAD steps
-    RowsUnit cur = unit_info(u_first);
-    RowsUnit nxt = (u_first + 1 < u_end) ? unit_info(u_first + 1) : cur;
-    UnitBlocks cub = unit_blocks(cur, true);
-    UnitBlocks nub = unit_blocks(nxt, u_first + 1 < u_end);
+    // prologue: Q of the first sequence, then the first AHEAD steps (a unit has >= 2)
     issue_q(cur.b, cur.h0, 0);
-    int last_q_step = 0;                     // step whose loads included the latest Q staging
-    int nseg_issued = 1;                     // sequences staged so far (segment i uses s_vs[i & 1])
-    int vs_buf = 1;                          // s_vs buffer of the current segment
-#pragma unroll
-    for (int r = 0; r < AHEAD; ++r) issue(r, r % NST, cur, cub, true);
-    int prev_v = -1;                         // virtual sequence of the previous unit
-    int step0 = 0;                           // global step index of the unit's first step
+    int last_q_step = 0;                     // step whose loads followed the latest Q staging
+    int nseg_issued = 1;                     // sequences staged so far (segment i uses buffer i & 1)
+    int vs_buf = 1;
+    issue(cur, 0, 0);
+    issue(cur, 1, 1);
+    int gs = 0;                              // global step index (ring position)
+    int prev_v = -1;
 
-    for (int u = u_first; u < u_end; ++u, step0 += STEPS) {
-        const bool seg_start = (cur.v != prev_v);
-        if (seg_start) vs_buf ^= 1;
-        const bool next_ok = (u + 1 < u_end);
-        const bool next_new_seg = next_ok && (nxt.v != cur.v);
-        const bool active = (w >= cur.hlo && w < cur.hhi);
-        const int h = cur.h0 + w;            // this wave's KV head in the unit
-        float sv[NRB][NCH][8];
-        uint32_t p8[NRB][NCH][2];             // FP8 codes of 448 P for the whole tile
+    // one step: wait for its loads, barrier, keep AHEAD steps in flight
+    auto step_begin = [&](int idx) {
+        if (last_q_step == gs + 1)
+            wait_vm<PER_STEP * (AHEAD - 1) + QNW>();
+        else
+            wait_vm<PER_STEP * (AHEAD - 1)>();
+        barrier_nofence();
+        const int nidx = idx + AHEAD, st = (gs + AHEAD) % NST;
+        if (nidx < 2 * cur.nvs) {
+            issue(cur, nidx, st);
+        } else {
+            const int k = nidx - 2 * cur.nvs;   // 0 or 1; the next unit has >= 2 steps
+            if (k == 0 && nxt.nvs > 0 && nxt.v != cur.v) {
+                issue_q(nxt.b, nxt.h0, nseg_issued & 1);
+                ++nseg_issued;
+                last_q_step = gs + AHEAD;
+            }
+            issue(nxt, k, st);
+        }
+    };
+
+    while (true) {
+        const bool seg_start = cur.v != prev_v;
+        if (seg_start) {
+            vs_buf ^= 1;
+            seg_t0 = cur.t;
+        }
+        const int h = cur.h0 + hl;
+        float sv[NRB][NQ][8];
+        uint32_t p8[NRB][NQ][2];
         float rmax[NRB], mt_s[NRB], mt_o[NRB][4], lsum[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
@@ -340,158 +377,144 @@ __global__ __launch_bounds__(HG * 64) void decode_rows_kernel(DecodeParams a) {
             lsum[rb] = 0.f;
         }
 
+        // ---------------- K pass: steps 2-4, S = q8 . k8 * scales, masked -------------------------
 #pragma unroll
-        for (int r = 0; r < STEPS; ++r) {
-            const int step = step0 + r;
-            const int st = step % NST;
-            // ---- wait for this step's chunk (own loads), then for every wave -----------
-            // Loads complete in issue order; the ones issued after this step's are the
-            // chunk loads of the next AHEAD-1 steps, plus QNW Q-staging loads if those
-            // were issued with one of them.
-            if (last_q_step > step && last_q_step <= step + AHEAD - 1)
-                wait_vm<PER_STEP * (AHEAD - 1) + QNW>();
-            else
-                wait_vm<PER_STEP * (AHEAD - 1)>();
-            barrier_nofence();
-            // ---- keep AHEAD chunks in flight: issue step + AHEAD ------------------------
-            {
-                const int rn = r + AHEAD;
-                if (rn < STEPS) {
-                    issue(rn, (step + AHEAD) % NST, cur, cub, true);
-                } else {
-                    if (rn == STEPS && next_new_seg) {
-                        issue_q(nxt.b, nxt.h0, nseg_issued & 1);   // staged with the next unit's first step
-                        ++nseg_issued;
-                        last_q_step = step + AHEAD;
-                    }
-                    issue(rn - STEPS, (step + AHEAD) % NST, nxt, nub, next_ok);
-                }
-            }
-            const uint8_t* ring = s_ring[st];
-            const int c = r < NCH ? r : r - NCH;
-            const int p0 = cur.t * T + 32 * c;
-            const bool valid = p0 < cur.seq;
-
-            if (r == 0 && seg_start) {
-                // ---- step 1: this head's query rows -> bf16 operands of exact FP8 codes
+        for (int r = 0; r < NBLK; ++r) {
+            if (r < cur.nvs) {
+                step_begin(r);
+                const uint8_t* ring = s_ring[gs % NST];
+                const float* ksr = s_ks[gs % NST][w];
+                if (r == 0 && seg_start) {
+                    // step 1: this head's query rows -> bf16 operands of exact FP8 codes
 #pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const int rr = rb * 16 + lr;
-                    uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                    qcoef[rb] = 0.f;
-                    if (rr < a.rows) {
-                        const int s = rr / a.G, gq = rr % a.G;
-                        const int qi = s * a.nq + h * a.G + gq;        // row inside the staged block
-                        const float qs = s_qs[qi];
-                        qcoef[rb] = qs * a.softmax_scale * kLog2e;
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        const int rr = rb * 16 + lr;
+                        uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                        qcoef[rb] = 0.f;
+                        if (rr < rows) {
+                            const int sr = hl * rows + rr;
+                            const float qs = s_qs[vs_buf][sr];
+                            qcoef[rb] = qs * a.softmax_scale * kLog2e;
 #pragma unroll
-                        for (int hlf = 0; hlf < 2; ++hlf) {
-                            const uint8_t* qp = s_q + qi * 256 + (hlf * 64 + 16 * lg) * 2;
-                            const i32x4 v0 = *reinterpret_cast<const i32x4*>(qp);
-                            const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + 16);
-                            const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
-                                                     (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
-                            quantise_q16(raw, qs, &wds[hlf * 4]);
+                            for (int hlf = 0; hlf < 2; ++hlf) {
+                                const uint8_t* qp = s_q[vs_buf] + sr * 256 + (hlf * 64 + 16 * lg) * 2;
+                                const i32x4 v0 = *reinterpret_cast<const i32x4*>(qp);
+                                const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + 16);
+                                const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
+                                                         (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
+                                quantise_q16(raw, qs, &wds[hlf * 4]);
+                            }
+                            if (DBG && a.dbg_q8 && p == 0) {
+                                const int s = rr / a.G, gq = rr - s * a.G;
+                                const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
+                                uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;
+#pragma unroll
+                                for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i)
+                                        *reinterpret_cast<uint32_t*>(dst + hlf * 64 + 16 * lg + 4 * i) = wds[hlf * 4 + i];
+                            }
                         }
-                        if (DBG && a.dbg_q8) {
-                            const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
-                            uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;
 #pragma unroll
-                            for (int hlf = 0; hlf < 2; ++hlf)
+                        for (int i = 0; i < 4; ++i) qop[rb][i] = fp8x8_to_op(wds[2 * i], wds[2 * i + 1]);
+                        M_s[rb] = -INFINITY;
+                        L_s[rb] = 0.f;
 #pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    *reinterpret_cast<uint32_t*>(dst + hlf * 64 + 16 * lg + 4 * i) = wds[hlf * 4 + i];
-                        }
+                        for (int i = 0; i < 4; ++i) M_o[rb][i] = -INFINITY;
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc) O[rb][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) qop[rb][i] = fp8x8_to_op(wds[2 * i], wds[2 * i + 1]);
-                    M_s[rb] = -INFINITY;
-                    L_s[rb] = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) M_o[rb][i] = -INFINITY;
-#pragma unroll
-                    for (int cc = 0; cc < 8; ++cc) O[rb][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                has_state = false;
-            }
-
-            if (r < NCH) {
-                // ---- steps 2-4: S^T = K Q^T, dequantise, mask ----------------------------
-                if (active && valid) {
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int q = 2 * r + cc;                      // chunk of this wave in the tile
+                    const int tb = 64 * p + 32 * cc;               // first token of the chunk in the block
+                    const int p0 = cur.t * T + r * kStepTok + tb;  // its logical position
                     if (DBG && a.dbg_rows && h == 0 && lg == 0) {
-                        const int64_t s0 = cub.row0[c / 4] + 32 * (c % 4);
+                        const int64_t s0 = (int64_t)__builtin_amdgcn_readlane(cur.ids, r) * kStepTok + tb;
 #pragma unroll
                         for (int k = 0; k < 2; ++k)
                             if (p0 + 16 * k + lr < cur.seq)
                                 a.dbg_rows[(int64_t)cur.b * a.capacity + p0 + 16 * k + lr] = (int32_t)(s0 + 16 * k + lr);
                     }
-                    float ks[8];
-                    {
-                        const f32x4 k0 = *reinterpret_cast<const f32x4*>(&s_ks[st][w][4 * lg]);
-                        const f32x4 k1 = *reinterpret_cast<const f32x4*>(&s_ks[st][w][16 + 4 * lg]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            ks[i] = k0[i];
-                            ks[4 + i] = k1[i];
-                        }
-                    }
+                    const f32x4 k0 = *reinterpret_cast<const f32x4*>(&ksr[32 * cc + 4 * lg]);
+                    const f32x4 k1 = *reinterpret_cast<const f32x4*>(&ksr[32 * cc + 16 + 4 * lg]);
 #pragma unroll
                     for (int k = 0; k < 2; ++k) {
-                        const i32x4 lo = *reinterpret_cast<const i32x4*>(ring + kslot[0] + k * TOK16);
-                        const i32x4 hi = *reinterpret_cast<const i32x4*>(ring + kslot[1] + k * TOK16);
+                        const i32x4 klo = *reinterpret_cast<const i32x4*>(ring + kslot[0] + (tb + 16 * k) * TOKB);
+                        const i32x4 khi = *reinterpret_cast<const i32x4*>(ring + kslot[1] + (tb + 16 * k) * TOKB);
                         f32x4 acc[NRB];
 #pragma unroll
                         for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const bf16x8 kop = (i < 2) ? fp8x8_to_op((uint32_t)lo[2 * i], (uint32_t)lo[2 * i + 1])
-                                                       : fp8x8_to_op((uint32_t)hi[2 * i - 4], (uint32_t)hi[2 * i - 3]);
+                            const bf16x8 kop = (i < 2) ? fp8x8_to_op((uint32_t)klo[2 * i], (uint32_t)klo[2 * i + 1])
+                                                       : fp8x8_to_op((uint32_t)khi[2 * i - 4], (uint32_t)khi[2 * i - 3]);
 #pragma unroll
                             for (int rb = 0; rb < NRB; ++rb) acc[rb] = mfma_bf16(kop, qop[rb][i], acc[rb]);
                         }
+                        const f32x4 kk = k ? k1 : k0;
 #pragma unroll
                         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) sv[rb][c][4 * k + i] = acc[rb][i] * ks[4 * k + i] * qcoef[rb];
+                            for (int i = 0; i < 4; ++i) sv[rb][q][4 * k + i] = acc[rb][i] * kk[i] * qcoef[rb];
                     }
                     if (p0 + 32 > cur.seq) {
 #pragma unroll
                         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
                             for (int j = 0; j < 8; ++j)
-                                sv[rb][c][j] = (p0 + chunk_token(lg, j) < cur.seq) ? sv[rb][c][j] : -INFINITY;
+                                sv[rb][q][j] = (p0 + chunk_token(lg, j) < cur.seq) ? sv[rb][q][j] : -INFINITY;
                     }
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) rmax[rb] = fmaxf(rmax[rb], sv[rb][c][j]);
-                } else {
-#pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) sv[rb][c][j] = -INFINITY;
+                        for (int j = 0; j < 8; ++j) rmax[rb] = fmaxf(rmax[rb], sv[rb][q][j]);
                 }
+                ++gs;
+            } else {
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) sv[rb][2 * r + cc][j] = -INFINITY;
+            }
+        }
+        // this half's row maxima; the partner's arrive through LDS by the next barrier
+        float mown[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            mown[rb] = wave_max_over_groups(rmax[rb]);
+            if (lg == 0) s_max[w][rb * 16 + lr] = mown[rb];
+        }
 
-                if (r == NCH - 1 && active) {
-                    // ---- step 5a: tile max per row; O <- O * exp2(M_old - m_tile) ----------
+        // ---------------- V pass: steps 5-7, P, its per-tile FP8 codes, P.V -------------------------
+#pragma unroll
+        for (int r = 0; r < NBLK; ++r) {
+            if (r < cur.nvs) {
+                step_begin(cur.nvs + r);
+                const uint8_t* ring = s_ring[gs % NST];
+                if (r == 0) {
+                    // step 5a: tile max per row; O <- O * exp2(M_old - m_tile)
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb) {
-                        const float m = wave_max_over_groups(rmax[rb]);
+                        const float m = fmaxf(mown[rb], s_max[w ^ 1][rb * 16 + lr]);
                         mt_s[rb] = m;
                         // P' = 448 exp2(S - m_tile) = exp2(S + off); a dropped row gets off = -inf
                         const float poff = (M_s[rb] - m > kDropLog2) ? -INFINITY : kLog2_448 - m;
-                        // steps 5b-6 for the whole tile: the FP8 code of P' (the tile's max maps
-                        // to 448) and the running sum of the unquantised P'
+                        // steps 5b-6 for this half of the tile: the FP8 code of P' (the tile's
+                        // max maps to 448) and the running sum of the unquantised P'
 #pragma unroll
-                        for (int cc = 0; cc < NCH; ++cc) {
+                        for (int q = 0; q < NQ; ++q) {
                             float pv[8];
 #pragma unroll
                             for (int j = 0; j < 8; ++j) {
-                                pv[j] = __builtin_amdgcn_exp2f(sv[rb][cc][j] + poff);
+                                pv[j] = __builtin_amdgcn_exp2f(sv[rb][q][j] + poff);
                                 lsum[rb] += pv[j];
                             }
-                            p8[rb][cc][0] = cvt4_fp8(pv[0], pv[1], pv[2], pv[3]);
-                            p8[rb][cc][1] = cvt4_fp8(pv[4], pv[5], pv[6], pv[7]);
+                            p8[rb][q][0] = cvt4_fp8(pv[0], pv[1], pv[2], pv[3]);
+                            p8[rb][q][1] = cvt4_fp8(pv[4], pv[5], pv[6], pv[7]);
                         }
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
@@ -504,13 +527,15 @@ __global__ __launch_bounds__(HG * 64) void decode_rows_kernel(DecodeParams a) {
                         }
                     }
                 }
-            } else {
-                // ---- steps 5b-7: P, per-tile FP8 quantisation, P.V -------------------------
-                if (active && valid) {
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int q = 2 * r + cc;
+                    const int tb = 64 * p + 32 * cc;
+                    const int p0 = cur.t * T + r * kStepTok + tb;
                     uint32_t xl[8], xh[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const uint2 x = *reinterpret_cast<const uint2*>(ring + vaddr[j & 3] + (j >> 2) * TOK16);
+                        const uint2 x = *reinterpret_cast<const uint2*>(ring + vaddr[j & 3] + (tb + 16 * (j >> 2)) * TOKB);
                         xl[j] = x.x;
                         xh[j] = x.y;
                     }
@@ -530,204 +555,258 @@ __global__ __launch_bounds__(HG * 64) void decode_rows_kernel(DecodeParams a) {
                     transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
                     bf16x8 pop[NRB];
 #pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) pop[rb] = fp8x8_to_op(p8[rb][c][0], p8[rb][c][1]);
+                    for (int rb = 0; rb < NRB; ++rb) pop[rb] = fp8x8_to_op(p8[rb][q][0], p8[rb][q][1]);
 #pragma unroll
-                    for (int cc = 0; cc < 8; ++cc) {
-                        const bf16x8 vop = fp8x8_to_op(ylo[cc], yhi[cc]);
+                    for (int c8 = 0; c8 < 8; ++c8) {
+                        const bf16x8 vop = fp8x8_to_op(ylo[c8], yhi[c8]);
 #pragma unroll
-                        for (int rb = 0; rb < NRB; ++rb) O[rb][cc] = mfma_bf16(pop[rb], vop, O[rb][cc]);
+                        for (int rb = 0; rb < NRB; ++rb) O[rb][c8] = mfma_bf16(pop[rb], vop, O[rb][c8]);
                     }
                 }
-
-                if (r == STEPS - 1 && active) {
-                    // ---- steps 8-9: finish the rescale, update the running state -----------
+                ++gs;
+            }
+        }
+        // ---- steps 8-9: finish the rescale, update the running state --------------------------
 #pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) {
-                        const float mn = fmaxf(M_s[rb], mt_s[rb]);
-                        L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) +
-                                  lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
-                        M_s[rb] = mn;
+        for (int rb = 0; rb < NRB; ++rb) {
+            const float mn = fmaxf(M_s[rb], mt_s[rb]);
+            L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) + lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
+            M_s[rb] = mn;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float mo = fmaxf(M_o[rb][i], mt_o[rb][i]);
-                            const float d = M_o[rb][i] - mt_o[rb][i];
-                            const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
-                            M_o[rb][i] = mo;
+            for (int i = 0; i < 4; ++i) {
+                const float mo = fmaxf(M_o[rb][i], mt_o[rb][i]);
+                const float d = M_o[rb][i] - mt_o[rb][i];
+                const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
+                M_o[rb][i] = mo;
 #pragma unroll
-                            for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
-                        }
-                    }
-                    has_state = true;
-                }
+                for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
             }
         }
 
-        // ---- end of a (virtual sequence, head) segment: finish in place or write a partial --
-        const bool seg_end = !next_ok || next_new_seg;
-        if (seg_end && has_state) {
-            const int b = cur.b;
-            const int pv0 = __builtin_amdgcn_readfirstlane(s_pref[cur.v]);
-            const int64_t nb = __builtin_amdgcn_readfirstlane(s_pref[cur.v + 1]) - pv0;
-            const int64_t af = (int64_t)pv0 * HG + w, al = (pv0 + nb - 1) * HG + w;
-            const int64_t gf = ((af + 1) * Geff - 1) / A, gl = ((al + 1) * Geff - 1) / A;
-            const int count = (int)(gl - gf + 1);
-            const int k = (int)(g - gf);
-            float Lw[NRB];
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) Lw[rb] = wave_sum_over_groups(L_s[rb]);
-            const f32x4 vs0 = *reinterpret_cast<const f32x4*>(&s_vs[vs_buf][w][8 * lr]);
-            const f32x4 vs1 = *reinterpret_cast<const f32x4*>(&s_vs[vs_buf][w][8 * lr + 4]);
+        // ---- end of a (batch, group) segment in this workgroup --------------------------------
+        const bool seg_end = nxt.nvs == 0 || nxt.v != cur.v;
+        if (seg_end) {
+            const int nt = ntiles(cur.v);
+            const bool split = owner(mid_of(cur.v, 0)) != owner(mid_of(cur.v, nt - 1));
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
+                // the two halves of each head: wave p = 1 hands its O and L to wave p = 0
+                float Lw = wave_sum_over_groups(L_s[rb]);
+                if (p == 1) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = rb * 16 + 4 * lg + i;
-                    const float Lr = __shfl(Lw[rb], 4 * lg + i, 64);
-                    if (rr >= a.rows) continue;
-                    const int s = rr / a.G, gq = rr % a.G;
-                    const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
-                    if (count == 1) {
-                        // step 10: out = O * v_scale / L' (L' = 448 L), bf16
-                        const float inv = 1.f / Lr;
-                        uint32_t pk[4];
+                    for (int i = 0; i < 4; ++i) {
+                        float* dst = &s_comb[hl][(4 * lg + i) * kHeadDim + 8 * lr];
+                        *reinterpret_cast<f32x4*>(dst) = f32x4{O[rb][0][i], O[rb][1][i], O[rb][2][i], O[rb][3][i]};
+                        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{O[rb][4][i], O[rb][5][i], O[rb][6][i], O[rb][7][i]};
+                    }
+                    if (lg == 0) s_comb[hl][16 * kHeadDim + lr] = Lw;
+                }
+                wait_lgkm();
+                barrier_nofence();
+                if (p == 0) {
 #pragma unroll
-                        for (int q2 = 0; q2 < 4; ++q2) {
-                            const int c0 = 2 * q2, c1 = 2 * q2 + 1;
-                            const float x0 = O[rb][c0][i] * (c0 < 4 ? vs0[c0] : vs1[c0 - 4]) * inv;
-                            const float x1 = O[rb][c1][i] * (c1 < 4 ? vs0[c1] : vs1[c1 - 4]) * inv;
-                            pk[q2] = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+                    for (int i = 0; i < 4; ++i) {
+                        const float* src = &s_comb[hl][(4 * lg + i) * kHeadDim + 8 * lr];
+                        const f32x4 o0 = *reinterpret_cast<const f32x4*>(src);
+                        const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc) {
+                            O[rb][cc][i] += o0[cc];
+                            O[rb][4 + cc][i] += o1[cc];
                         }
-                        *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + 8 * lr) =
-                            i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-                    } else {
-                        const int64_t slot = ((int64_t)b * a.nkv + h) * a.rows_kmax + k;
-                        float* po = a.part_o + (slot * R + rr) * kHeadDim + 8 * lr;
-                        *reinterpret_cast<f32x4*>(po) = f32x4{O[rb][0][i], O[rb][1][i], O[rb][2][i], O[rb][3][i]};
-                        *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[rb][4][i], O[rb][5][i], O[rb][6][i], O[rb][7][i]};
-                        if (lr == 0) {
-                            float* pm = a.part_ml + (slot * R + rr) * 2;
-                            pm[0] = M_o[rb][i];
-                            pm[1] = Lr;
+                    }
+                    Lw += s_comb[hl][16 * kHeadDim + lr];
+                    const f32x4 vs0 = *reinterpret_cast<const f32x4*>(&s_vs[vs_buf][hl * kHeadDim + 8 * lr]);
+                    const f32x4 vs1 = *reinterpret_cast<const f32x4*>(&s_vs[vs_buf][hl * kHeadDim + 8 * lr + 4]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = rb * 16 + 4 * lg + i;
+                        const float Lr = __shfl(Lw, 4 * lg + i, 64);
+                        if (rr >= rows) continue;
+                        const int s = rr / a.G, gq = rr - s * a.G;
+                        const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
+                        if (!split) {
+                            // step 10: out = O * v_scale / L' (L' = 448 L), bf16
+                            const float inv = 1.f / Lr;
+                            uint32_t pk[4];
+#pragma unroll
+                            for (int q2 = 0; q2 < 4; ++q2) {
+                                const int c0 = 2 * q2, c1 = 2 * q2 + 1;
+                                const float x0 = O[rb][c0][i] * (c0 < 4 ? vs0[c0] : vs1[c0 - 4]) * inv;
+                                const float x1 = O[rb][c1][i] * (c1 < 4 ? vs0[c1] : vs1[c1 - 4]) * inv;
+                                pk[q2] = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+                            }
+                            *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + 8 * lr) =
+                                i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+                        } else {
+                            const int64_t slot = ((int64_t)cur.b * nkv + h) * a.rows_kmax + seg_t0;
+                            float* po = a.part_o + (slot * R + rr) * kHeadDim + 8 * lr;
+                            *reinterpret_cast<f32x4*>(po) = f32x4{O[rb][0][i], O[rb][1][i], O[rb][2][i], O[rb][3][i]};
+                            *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[rb][4][i], O[rb][5][i], O[rb][6][i], O[rb][7][i]};
+                            if (lr == 0) {
+                                float* pm = a.part_ml + (slot * R + rr) * 2;
+                                pm[0] = M_o[rb][i];
+                                pm[1] = Lr;
+                            }
                         }
                     }
                 }
+                if (NRB > 1) {                        // s_comb is reused by the next row block
+                    wait_lgkm();
+                    barrier_nofence();
+                }
             }
-            has_state = false;
         }
 
         prev_v = cur.v;
+        if (nxt.nvs == 0) break;
         cur = nxt;
-        cub = nub;
-        if (u + 2 < u_end) {
-            nxt = unit_info(u + 2);
-            nub = unit_blocks(nxt, true);
-        }
+        nxt = next_unit(cur);
     }
-    // drain the ring before the workgroup retires (padding loads may still be in flight)
+    // drain the ring before the workgroup retires (loads past the last unit may be in flight)
     wait_vm<0>();
 }
 
-// Merge the partials of every (batch, KV head) that several workgroups worked on,
-// in workgroup order (deterministic).  One wave per output row.
-__global__ __launch_bounds__(256) void merge_rows_kernel(DecodeParams a, int R, int HG) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // over B * nkv * rows
-    const int64_t total = (int64_t)a.B * a.nkv * a.rows;
-    if (row_id >= total) return;
-    const int rr = (int)(row_id % a.rows);
-    const int bh = (int)(row_id / a.rows);
-    const int b = bh / a.nkv, h = bh % a.nkv;
-    const int NG = a.nkv / HG, BV = a.B * NG;
-    const int v = b * NG + h / HG, hl = h % HG;
+// Merge of the partials of the split (batch, group) pairs: one workgroup per pair.
+// The partition is recomputed from what the decode kernel published (cost prefix
+// and workgroup count): workgroup g of the decode owns the tiles whose cost
+// midpoints lie in [g C / Geff, (g + 1) C / Geff) and wrote its partial of each of
+// the group's heads into the slot of its first tile.  16 threads per (head, row).
+template <int NBLK, int HG>
+__global__ __launch_bounds__(256) void merge_rows_kernel(DecodeParams a, int R) {
+    __shared__ int s_tf[257];
+    const int B = a.B, NG = a.nkv / HG, BV = B * NG;
+    const int v = blockIdx.x;
     const int* meta = a.rows_meta;
-    const int U = meta[BV], Geff = meta[BV + 1];
-    const int nb = meta[v + 1] - meta[v];
-    if (nb == 0 || Geff <= 0) return;
-    const int64_t A = (int64_t)U * HG;
-    const int64_t af = (int64_t)meta[v] * HG + hl, al = ((int64_t)meta[v] + nb - 1) * HG + hl;
-    const int64_t gf = ((af + 1) * Geff - 1) / A, gl = ((al + 1) * Geff - 1) / A;
-    const int count = (int)(gl - gf + 1);
-    if (count <= 1) return;
-    const int64_t slot0 = ((int64_t)b * a.nkv + h) * a.rows_kmax;
-    float Ms = -INFINITY;
-    for (int k = 0; k < count; ++k) Ms = fmaxf(Ms, a.part_ml[((slot0 + k) * R + rr) * 2]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int k = 0; k < count; ++k) {
-        const float* pm = a.part_ml + ((slot0 + k) * R + rr) * 2;
-        const float f = __builtin_amdgcn_exp2f(pm[0] - Ms);
-        L += pm[1] * f;
-        const float2 o = *reinterpret_cast<const float2*>(a.part_o + ((slot0 + k) * R + rr) * kHeadDim + 2 * lane);
-        o0 += o.x * f;
-        o1 += o.y * f;
+    const int64_t C = meta[BV];
+    const int Geff = meta[BV + 1];
+    if (C <= 0 || Geff <= 0) return;
+    const int b = v / NG, h0 = (v - b * NG) * HG;
+    int seq = a.seqs[b];
+    seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
+    constexpr int T = NBLK * kStepTok;
+    const int nt = (seq + T - 1) / T, nb = (seq + kStepTok - 1) / kStepTok;
+    if (nt == 0) return;
+    const int64_t pv = meta[v];
+    auto mid_of = [&](int t) -> int64_t { return pv + 2LL * NBLK * t + min(NBLK, nb - t * NBLK); };
+    auto owner = [&](int64_t x) -> int { return (int)(((x + 1) * Geff - 1) / C); };
+    const int g0 = owner(mid_of(0)), g1 = owner(mid_of(nt - 1));
+    if (g0 == g1) return;                      // finished in place by the decode kernel
+    const int n = g1 - g0 + 1;                 // <= the decode grid
+    for (int i = threadIdx.x; i <= n; i += 256) {
+        int tf = nt;
+        if (i == 0) {
+            tf = 0;
+        } else if (i < n) {
+            // first tile whose midpoint is >= the start of workgroup g0 + i's range
+            const int64_t x = (int64_t)(g0 + i) * C / Geff;
+            const int64_t d = x - pv - NBLK;
+            int t = d <= 0 ? 0 : (int)min((int64_t)nt, (d + 2 * NBLK - 1) / (2 * NBLK));
+            while (t > 0 && mid_of(t - 1) >= x) --t;
+            while (t < nt && mid_of(t) < x) ++t;
+            tf = t;
+        }
+        s_tf[i] = tf;
     }
-    const int s = rr / a.G, gq = rr % a.G;
-    const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
-    const float* vs = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim;
-    const uint16_t r0 = f32_to_bf16_rne(o0 * vs[2 * lane] / L);
-    const uint16_t r1 = f32_to_bf16_rne(o1 * vs[2 * lane + 1] / L);
-    *reinterpret_cast<uint32_t*>(a.out + qrow * kHeadDim + 2 * lane) = (uint32_t)r0 | ((uint32_t)r1 << 16);
+    __syncthreads();
+    const int rows = a.rows;
+    const int sub = threadIdx.x & 15, d0 = 8 * sub;
+    for (int it = threadIdx.x >> 4; it < HG * rows; it += 16) {
+        const int hh = it / rows, rr = it - hh * rows;
+        const int h = h0 + hh;
+        const int64_t base = ((int64_t)b * a.nkv + h) * a.rows_kmax;
+        float Mx = -INFINITY, L = 0.f;
+        f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+        constexpr int SB = 4;                  // segments whose loads are issued together
+        for (int i0 = 0; i0 < n; i0 += SB) {
+            float m[SB], l[SB];
+            f32x4 x0[SB], x1[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int i = i0 + j;
+                const bool ok = i < n && s_tf[i] < s_tf[i + 1];
+                const int64_t slot = base + (ok ? s_tf[i] : 0);
+                const float* pm = a.part_ml + (slot * R + rr) * 2;
+                const float* po = a.part_o + (slot * R + rr) * kHeadDim + d0;
+                m[j] = ok ? pm[0] : -INFINITY;
+                l[j] = pm[1];
+                x0[j] = *reinterpret_cast<const f32x4*>(po);
+                x1[j] = *reinterpret_cast<const f32x4*>(po + 4);
+            }
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                if (m[j] == -INFINITY) continue;
+                // running merge in segment order: rescale to the larger maximum
+                const float mn = fmaxf(Mx, m[j]);
+                const float fa = __builtin_amdgcn_exp2f(Mx - mn), fb = __builtin_amdgcn_exp2f(m[j] - mn);
+                L = L * fa + l[j] * fb;
+                o0 = o0 * fa + x0[j] * fb;
+                o1 = o1 * fa + x1[j] * fb;
+                Mx = mn;
+            }
+        }
+        const float* vsp = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim + d0;
+        const f32x4 vs0 = *reinterpret_cast<const f32x4*>(vsp);
+        const f32x4 vs1 = *reinterpret_cast<const f32x4*>(vsp + 4);
+        const int sq = rr / a.G, gq = rr - sq * a.G;
+        const int64_t qrow = ((int64_t)b * a.s1 + sq) * a.nq + h * a.G + gq;
+        const float inv = 1.f / L;
+        uint32_t pk[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float y0 = (c < 2 ? o0[2 * c] : o1[2 * c - 4]) * (c < 2 ? vs0[2 * c] : vs1[2 * c - 4]) * inv;
+            const float y1 = (c < 2 ? o0[2 * c + 1] : o1[2 * c - 3]) * (c < 2 ? vs0[2 * c + 1] : vs1[2 * c - 3]) * inv;
+            pk[c] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+        }
+        *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + d0) = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+    }
 }
 
 // ------------------------------------------------------------------ dispatch
 
-// Ring stages of the four-head kernel: 16 KB each; six keep 80 KB of loads in
-// flight per CU within the 160 KB of LDS.
-#ifndef PA_ROWS_NST4
-#define PA_ROWS_NST4 6
-#endif
+// Heads per workgroup: two when nkv is even (four waves, one per SIMD), else one.
+int rows_group(int nkv) { return nkv % 2 == 0 ? 2 : 1; }
 
-// Heads per workgroup: one wave per head, at most four (one wave per SIMD, so
-// each wave has the 256 VGPRs that a 512-token score tile needs).
-int rows_group(int nkv) { return nkv >= 4 ? 4 : nkv; }
-
-template <int NRB, int NCH, int HG, int NST>
+template <int NRB, int NBLK, int HG>
 static hipError_t launch_rows_t(const DecodeParams& p, int grid, hipStream_t st, bool dbg) {
     if (dbg)
-        hipLaunchKernelGGL((decode_rows_kernel<NRB, NCH, HG, NST, true>), dim3(grid), dim3(HG * 64), 0, st, p);
+        hipLaunchKernelGGL((decode_rows_kernel<NRB, NBLK, HG, true>), dim3(grid), dim3(2 * HG * 64), 0, st, p);
     else
-        hipLaunchKernelGGL((decode_rows_kernel<NRB, NCH, HG, NST, false>), dim3(grid), dim3(HG * 64), 0, st, p);
+        hipLaunchKernelGGL((decode_rows_kernel<NRB, NBLK, HG, false>), dim3(grid), dim3(2 * HG * 64), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int BV = p.B * (p.nkv / HG);
+    hipLaunchKernelGGL((merge_rows_kernel<NBLK, HG>), dim3(BV), dim3(256), 0, st, p, NRB * 16);
     return hipGetLastError();
 }
 
-// Shapes of the whole-row path: (s2_tile, padded rows) in {128, 256} x {16, 32}
-// and 512 x 16.
-template <int HG, int NST>
+template <int HG>
 static hipError_t launch_rows_hg(const DecodeParams& p, int grid, hipStream_t st, bool dbg) {
-    const int nrb = (p.rows + 15) / 16;
+    const bool two = p.rows > 16;
     switch (p.s2_tile) {
-        case 128:
-            if (nrb == 1) return launch_rows_t<1, 4, HG, NST>(p, grid, st, dbg);
-            return launch_rows_t<2, 4, HG, NST>(p, grid, st, dbg);
-        case 256:
-            if (nrb == 1) return launch_rows_t<1, 8, HG, NST>(p, grid, st, dbg);
-            return launch_rows_t<2, 8, HG, NST>(p, grid, st, dbg);
-        default:
-            return launch_rows_t<1, 16, HG, NST>(p, grid, st, dbg);
+        case 128: return two ? launch_rows_t<2, 1, HG>(p, grid, st, dbg) : launch_rows_t<1, 1, HG>(p, grid, st, dbg);
+        case 256: return two ? launch_rows_t<2, 2, HG>(p, grid, st, dbg) : launch_rows_t<1, 2, HG>(p, grid, st, dbg);
+        case 512: return two ? launch_rows_t<2, 4, HG>(p, grid, st, dbg) : launch_rows_t<1, 4, HG>(p, grid, st, dbg);
+        default: return launch_rows_t<1, 8, HG>(p, grid, st, dbg);
     }
 }
 
+// Shapes of the whole-row path: any nkv; s2_tile 128-1024; up to 32 query rows per
+// KV head (16 for s2_tile 1024); at most kPrefixMax (batch, head group) pairs.
 bool rows_path_supported(int nkv, int s2_tile, int rows, int s1, int nq, int B) {
-    const int rpad = (rows + 15) / 16 * 16;
-    return (nkv == 1 || nkv == 2 || nkv == 4 || nkv == 8) && (s2_tile == 128 || s2_tile == 256 || s2_tile == 512) &&
-           rpad <= 32 && s2_tile * rpad <= 8192 && s1 * nq <= kQRowsMax &&
-           (int64_t)B * (nkv / rows_group(nkv)) <= kPrefixMax;
+    (void)s1;
+    (void)nq;
+    const bool tile_ok = s2_tile == 128 || s2_tile == 256 || s2_tile == 512 || (s2_tile == 1024 && rows <= 16);
+    return tile_ok && rows >= 1 && rows <= 32 && (int64_t)B * (nkv / rows_group(nkv)) <= kPrefixMax;
 }
 
 hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t st, bool dbg) {
-    hipError_t e;
-    const int hg = rows_group(p.nkv);
-    // one workgroup per CU for four heads (110 KB of LDS), else two
-    const int grid = cus * (hg == 4 ? 1 : 2);
-    switch (hg) {
-        case 1: e = launch_rows_hg<1, 4>(p, grid, st, dbg); break;
-        case 2: e = launch_rows_hg<2, 4>(p, grid, st, dbg); break;
-        default: e = launch_rows_hg<4, PA_ROWS_NST4>(p, grid, st, dbg); break;
-    }
-    if (e != hipSuccess) return e;
-    const int R = (p.rows + 15) / 16 * 16;
-    const int64_t total = (int64_t)p.B * p.nkv * p.rows;
-    hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, st, p, R, hg);
-    return hipGetLastError();
+    // one workgroup per CU (163 KB of LDS with two heads, 87 KB with one): the ranges
+    // have equal cost, so every workgroup must be resident at once
+    // (at most 256: the merge kernel's table of one sequence's workgroups holds 256)
+    const int grid = cus < 256 ? cus : 256;
+    if (rows_group(p.nkv) == 2) return launch_rows_hg<2>(p, grid, st, dbg);
+    return launch_rows_hg<1>(p, grid, st, dbg);
 }
 
 }  // namespace pa
