@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "fp8_paged_kv_amd", "csrc", "pa_fp8_decode.hip")
+KERNEL_SRC = os.path.join(ROOT, "fp8_paged_kv_amd", "csrc", "pa_fp8_decode_rows.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_glm45_config1_pmc.md")
 
 
@@ -202,7 +202,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "s1": cfg.s1, "nq": cfg.nq, "nkv": cfg.nkv, "D": cfg.D,
                    "block_size": cfg.block_size, "s2_tile": cfg.s2_tile, "seq_lens": "U[1024,8192] seed 1",
-                   "total_tokens": sum(seqs), "splits": nsplit, "rotating_input_sets": len(sets),
+                   "total_tokens": sum(seqs), "path": "whole-row" if args.splits == 0 else f"per-head, {nsplit} splits",
+                   "rotating_input_sets": len(sets),
                    "algorithmic_bytes_per_call": nbytes},
         "calls_per_s": round(1.0 / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -214,7 +215,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic), "traffic_note": traffic_note,
-                     "kernel": "pa::decode_kernel" + (" + pa::combine_kernel" if nsplit > 1 else "")},
+                     "kernel": ("pa::decode_rows_kernel + pa::merge_rows_kernel" if args.splits == 0
+                                else "pa::decode_kernel" + (" + pa::combine_kernel" if nsplit > 1 else ""))},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, sets, seqs, args.cpu_target_s)

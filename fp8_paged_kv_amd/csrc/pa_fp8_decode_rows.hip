@@ -667,33 +667,38 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     wait_vm<0>();
 }
 
-// Merge of the partials of the split (batch, group) pairs: one workgroup per pair.
-// The partition is recomputed from what the decode kernel published (cost prefix
-// and workgroup count): workgroup g of the decode owns the tiles whose cost
-// midpoints lie in [g C / Geff, (g + 1) C / Geff) and wrote its partial of each of
-// the group's heads into the slot of its first tile.  16 threads per (head, row).
+// Merge of the partials of split (batch, head) pairs: one workgroup per pair, 16
+// threads per query row (8 columns each).  The partition is recomputed from what
+// the decode kernel published (cost prefix and workgroup count): decode
+// workgroup g owns the tiles whose cost midpoints lie in [g C / Geff,
+// (g + 1) C / Geff) and wrote its partial into the slot of its first tile.
 template <int NBLK, int HG>
-__global__ __launch_bounds__(256) void merge_rows_kernel(DecodeParams a, int R) {
+__global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) {
     __shared__ int s_tf[257];
-    const int B = a.B, NG = a.nkv / HG, BV = B * NG;
-    const int v = blockIdx.x;
+    const int NG = a.nkv / HG, BV = a.B * NG;
+    const int bh = blockIdx.x, b = bh / a.nkv, h = bh - b * a.nkv;
+    const int v = b * NG + h / HG;
     const int* meta = a.rows_meta;
+    // independent loads first
     const int64_t C = meta[BV];
     const int Geff = meta[BV + 1];
-    if (C <= 0 || Geff <= 0) return;
-    const int b = v / NG, h0 = (v - b * NG) * HG;
+    const int64_t pv = meta[v];
     int seq = a.seqs[b];
+    const int sub = threadIdx.x & 15, d0 = 8 * sub, rr = threadIdx.x >> 4;
+    const float* vsp = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim + d0;
+    const f32x4 vs0 = *reinterpret_cast<const f32x4*>(vsp);
+    const f32x4 vs1 = *reinterpret_cast<const f32x4*>(vsp + 4);
+    if (C <= 0 || Geff <= 0) return;
     seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
     constexpr int T = NBLK * kStepTok;
     const int nt = (seq + T - 1) / T, nb = (seq + kStepTok - 1) / kStepTok;
     if (nt == 0) return;
-    const int64_t pv = meta[v];
     auto mid_of = [&](int t) -> int64_t { return pv + 2LL * NBLK * t + min(NBLK, nb - t * NBLK); };
     auto owner = [&](int64_t x) -> int { return (int)(((x + 1) * Geff - 1) / C); };
     const int g0 = owner(mid_of(0)), g1 = owner(mid_of(nt - 1));
     if (g0 == g1) return;                      // finished in place by the decode kernel
-    const int n = g1 - g0 + 1;                 // <= the decode grid
-    for (int i = threadIdx.x; i <= n; i += 256) {
+    const int n = g1 - g0 + 1;                 // <= the decode grid (<= 256)
+    for (int i = threadIdx.x; i <= n; i += blockDim.x) {
         int tf = nt;
         if (i == 0) {
             tf = 0;
@@ -709,57 +714,49 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeParams a, int R) 
         s_tf[i] = tf;
     }
     __syncthreads();
-    const int rows = a.rows;
-    const int sub = threadIdx.x & 15, d0 = 8 * sub;
-    for (int it = threadIdx.x >> 4; it < HG * rows; it += 16) {
-        const int hh = it / rows, rr = it - hh * rows;
-        const int h = h0 + hh;
-        const int64_t base = ((int64_t)b * a.nkv + h) * a.rows_kmax;
-        float Mx = -INFINITY, L = 0.f;
-        f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
-        constexpr int SB = 4;                  // segments whose loads are issued together
-        for (int i0 = 0; i0 < n; i0 += SB) {
-            float m[SB], l[SB];
-            f32x4 x0[SB], x1[SB];
+    if (rr >= a.rows) return;
+    const int64_t base = ((int64_t)b * a.nkv + h) * a.rows_kmax;
+    float Mx = -INFINITY, L = 0.f;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    constexpr int SB = 4;                      // segments whose loads are issued together
+    for (int i0 = 0; i0 < n; i0 += SB) {
+        float m[SB], l[SB];
+        f32x4 x0[SB], x1[SB];
 #pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int i = i0 + j;
-                const bool ok = i < n && s_tf[i] < s_tf[i + 1];
-                const int64_t slot = base + (ok ? s_tf[i] : 0);
-                const float* pm = a.part_ml + (slot * R + rr) * 2;
-                const float* po = a.part_o + (slot * R + rr) * kHeadDim + d0;
-                m[j] = ok ? pm[0] : -INFINITY;
-                l[j] = pm[1];
-                x0[j] = *reinterpret_cast<const f32x4*>(po);
-                x1[j] = *reinterpret_cast<const f32x4*>(po + 4);
-            }
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                if (m[j] == -INFINITY) continue;
-                // running merge in segment order: rescale to the larger maximum
-                const float mn = fmaxf(Mx, m[j]);
-                const float fa = __builtin_amdgcn_exp2f(Mx - mn), fb = __builtin_amdgcn_exp2f(m[j] - mn);
-                L = L * fa + l[j] * fb;
-                o0 = o0 * fa + x0[j] * fb;
-                o1 = o1 * fa + x1[j] * fb;
-                Mx = mn;
-            }
+        for (int j = 0; j < SB; ++j) {
+            const int i = i0 + j;
+            const bool ok = i < n && s_tf[i] < s_tf[i + 1];
+            const int64_t slot = base + (ok ? s_tf[i] : 0);
+            const float* pm = a.part_ml + (slot * R + rr) * 2;
+            const float* po = a.part_o + (slot * R + rr) * kHeadDim + d0;
+            m[j] = ok ? pm[0] : -INFINITY;
+            l[j] = pm[1];
+            x0[j] = *reinterpret_cast<const f32x4*>(po);
+            x1[j] = *reinterpret_cast<const f32x4*>(po + 4);
         }
-        const float* vsp = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim + d0;
-        const f32x4 vs0 = *reinterpret_cast<const f32x4*>(vsp);
-        const f32x4 vs1 = *reinterpret_cast<const f32x4*>(vsp + 4);
-        const int sq = rr / a.G, gq = rr - sq * a.G;
-        const int64_t qrow = ((int64_t)b * a.s1 + sq) * a.nq + h * a.G + gq;
-        const float inv = 1.f / L;
-        uint32_t pk[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float y0 = (c < 2 ? o0[2 * c] : o1[2 * c - 4]) * (c < 2 ? vs0[2 * c] : vs1[2 * c - 4]) * inv;
-            const float y1 = (c < 2 ? o0[2 * c + 1] : o1[2 * c - 3]) * (c < 2 ? vs0[2 * c + 1] : vs1[2 * c - 3]) * inv;
-            pk[c] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+        for (int j = 0; j < SB; ++j) {
+            if (m[j] == -INFINITY) continue;
+            // running merge in segment order: rescale to the larger maximum
+            const float mn = fmaxf(Mx, m[j]);
+            const float fa = __builtin_amdgcn_exp2f(Mx - mn), fb = __builtin_amdgcn_exp2f(m[j] - mn);
+            L = L * fa + l[j] * fb;
+            o0 = o0 * fa + x0[j] * fb;
+            o1 = o1 * fa + x1[j] * fb;
+            Mx = mn;
         }
-        *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + d0) = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
     }
+    const int sq = rr / a.G, gq = rr - sq * a.G;
+    const int64_t qrow = ((int64_t)b * a.s1 + sq) * a.nq + h * a.G + gq;
+    const float inv = 1.f / L;
+    uint32_t pk[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float y0 = (c < 2 ? o0[2 * c] : o1[2 * c - 4]) * (c < 2 ? vs0[2 * c] : vs1[2 * c - 4]) * inv;
+        const float y1 = (c < 2 ? o0[2 * c + 1] : o1[2 * c - 3]) * (c < 2 ? vs0[2 * c + 1] : vs1[2 * c - 3]) * inv;
+        pk[c] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+    }
+    *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + d0) = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -775,8 +772,8 @@ static hipError_t launch_rows_t(const DecodeParams& p, int grid, hipStream_t st,
         hipLaunchKernelGGL((decode_rows_kernel<NRB, NBLK, HG, false>), dim3(grid), dim3(2 * HG * 64), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int BV = p.B * (p.nkv / HG);
-    hipLaunchKernelGGL((merge_rows_kernel<NBLK, HG>), dim3(BV), dim3(256), 0, st, p, NRB * 16);
+    // one workgroup per (batch, head); 16 threads per query row
+    hipLaunchKernelGGL((merge_rows_kernel<NBLK, HG>), dim3(p.B * p.nkv), dim3(NRB * 256), 0, st, p, NRB * 16);
     return hipGetLastError();
 }
 
