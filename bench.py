@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "fp8_paged_kv_amd", "csrc", "pa_fp8_decode_rows.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_glm45_config1_pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_rows_kernel_glm45_b32_pmc.md")
 
 
 def kernel_hash() -> str:

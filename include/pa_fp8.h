@@ -23,10 +23,11 @@
  *    nothing and never synchronises the stream; work is enqueued on `stream`
  *    (a hipStream_t; NULL = the null stream) and returns immediately.
  *  - Inputs are read only.  Outputs are written completely.
- *  - Workspace (only when a call splits sequences): its first bytes hold one
- *    arrival counter per (batch, KV head).  They must be zero before the
- *    first call that uses the buffer (e.g. allocate it zero-filled); every
- *    call leaves them zero again.  The rest is scratch.
+ *  - Workspace (size from pa_fp8_decode_workspace_size): scratch for the
+ *    partial results of split sequences.  With an explicit split count its
+ *    first bytes hold one arrival counter per (batch, KV head), which must
+ *    be zero before the first call that uses the buffer (allocate it
+ *    zero-filled); every call leaves them zero again.
  *  - Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and a status != PA_OK is returned, with a
  *    message available from pa_fp8_last_error() (per host thread).
@@ -71,11 +72,11 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
  * contiguous groups):
  *   1  q8 = E4M3(q / q_scale) (round to nearest even, saturate at +-448);
  *   2  the tokens p < seq_b are read through block_table in tiles of s2_tile;
- *   3  S_raw = q8 . k8 (FP8 MFMA, FP32 accumulate);
+ *   3  S_raw = q8 . k8 (exact FP8 x FP8 products, FP32 accumulation);
  *   4  S = S_raw * q_scale * k_scale[p] * softmax_scale;
  *   5  running max M, running sum L += sum exp(S - M) (unquantised);
  *   6  per row and tile: P8 = E4M3(P * 448 / max_tile P);
- *   7  O_tile = P8 . v8 (FP8 MFMA);
+ *   7  O_tile = P8 . v8 (exact products, FP32 accumulation);
  *   8-9 O = O * exp(M_old - M_new) + O_tile * (max_tile P / 448) * v_scale;
  *   10 out = bf16(O / L).
  * Layouts:
@@ -94,9 +95,11 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
  * [0, max_blocks_per_seq * block_size]; seq_b == 0 gives zero output rows;
  * bytes of tokens p >= seq_b are never used (their values may be NaN).
  * Supported: D == 128, block_size == 128, s2_tile in {128, 256, 512, 1024,
- * 2048}, s1 * nq / nkv <= 64.  num_splits: 0 = auto, else the number of
- * contiguous tile ranges each sequence is split into (>= 1); splits > 1
- * need the workspace from pa_fp8_decode_workspace_size.
+ * 2048}, s1 * nq / nkv <= 64.  num_splits: 0 = the library's choice (a
+ * balanced split of the whole batch across the GPU when the shape allows
+ * it), else the number of contiguous tile ranges each sequence is split
+ * into (>= 1).  Whenever pa_fp8_decode_workspace_size reports a nonzero
+ * size, workspace_dev must hold at least that many bytes.
  */
 pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev,
                           const uint8_t* k_cache_dev, const float* k_scale_dev,
