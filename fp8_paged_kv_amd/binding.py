@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("PA_FP8_LIB") or os.path.join(PKG, "libpa_fp8.so")
 PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
 
 EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug",
+           "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode",
            "pa_fp8_last_error", "pa_fp8_version")
 
 
@@ -46,6 +47,10 @@ def lib():
         L.pa_fp8_decode_debug.restype = I
         L.pa_fp8_decode_workspace_size.argtypes = [I] * 9 + [P, P]
         L.pa_fp8_decode_workspace_size.restype = I
+        L.pa_fp8_mla_workspace_size.argtypes = [I] * 5 + [P]
+        L.pa_fp8_mla_workspace_size.restype = I
+        L.pa_fp8_mla_sparse_decode.argtypes = [P] * 7 + [I] * 7 + [F, I, P, Z, P]
+        L.pa_fp8_mla_sparse_decode.restype = I
         L.pa_fp8_last_error.argtypes = []
         L.pa_fp8_last_error.restype = ctypes.c_char_p
         L.pa_fp8_version.argtypes = []
@@ -143,3 +148,38 @@ def decode_inputs(inp: dict, num_splits=0, out=None, workspace=None, stream=None
                   inp["block_table"], inp["kv_act_seqs"], inp["softmax_scale"],
                   inp.get("s2_tile", inp["cfg"].s2_tile), num_splits=num_splits, out=out, workspace=workspace,
                   stream=stream, s1=inp["cfg"].s1)
+
+
+def mla_workspace_size(B, s1, nq, topk, s2_tile):
+    n = ctypes.c_size_t(0)
+    _check(lib().pa_fp8_mla_workspace_size(B, s1, nq, topk, s2_tile, ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode(q_nope, q_rope, cache, topk, block_table, kv_act_seqs, softmax_scale, s2_tile, s1,
+               out=None, workspace=None, stream=None, block_size=128):
+    """MLA sparse decode; returns out [B*s1*nq, 512] bf16 (allocated if not given)."""
+    B = int(kv_act_seqs.shape[0])
+    nq = int(q_nope.shape[0]) // (B * s1)
+    K = int(topk.shape[1])
+    _checked_inputs(dict(q_nope=q_nope, q_rope=q_rope, cache=cache, topk=topk, block_table=block_table,
+                         kv_act_seqs=kv_act_seqs, out=out, workspace=workspace))
+    if out is None:
+        out = torch.empty((B * s1 * nq, 512), dtype=torch.bfloat16, device=q_nope.device)
+    need = mla_workspace_size(B, s1, nq, K, s2_tile)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    _check(lib().pa_fp8_mla_sparse_decode(
+        _ptr(q_nope), _ptr(q_rope), _ptr(cache), _ptr(topk), _ptr(block_table), _ptr(kv_act_seqs), _ptr(out),
+        B, s1, nq, K, block_size, int(block_table.shape[1]), int(cache.shape[0]) // block_size,
+        float(softmax_scale), int(s2_tile), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def mla_decode_inputs(inp: dict, out=None, workspace=None, stream=None):
+    """mla_decode() on a dict produced by fp8_paged_kv_amd.synth.make_mla_inputs."""
+    cfg = inp["cfg"]
+    return mla_decode(inp["q_nope"], inp["q_rope"], inp["cache"], inp["topk"], inp["block_table"],
+                      inp["kv_act_seqs"], inp["softmax_scale"], inp.get("s2_tile", cfg.s2_tile), cfg.s1,
+                      out=out, workspace=workspace, stream=stream, block_size=cfg.block_size)

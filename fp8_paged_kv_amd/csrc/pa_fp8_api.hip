@@ -248,6 +248,75 @@ pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev, con
                true, stream);
 }
 
+pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_tile, size_t* bytes_host) {
+    g_err[0] = 0;
+    if (!bytes_host) return fail(PA_ERR_NULLPTR, "bytes_host is NULL");
+    if (B <= 0 || s1 <= 0 || nq <= 0 || topk <= 0 || s2_tile <= 0)
+        return fail(PA_ERR_INVALID, "sizes must be positive (B=%d s1=%d nq=%d topk=%d s2_tile=%d)", B, s1, nq,
+                    topk, s2_tile);
+    if (!pa::mla_supported(nq, s2_tile))
+        return fail(PA_ERR_UNSUPPORTED, "MLA decode built for nq a multiple of 32 and s2_tile 128/256/512 "
+                    "(nq=%d s2_tile=%d)", nq, s2_tile);
+    const size_t rows = (size_t)B * s1 * nq, nt = (size_t)((topk + s2_tile - 1) / s2_tile);
+    *bytes_host = align256(rows * nt * 2 * sizeof(float)) + rows * nt * 512 * sizeof(float);
+    return PA_OK;
+}
+
+pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_dev, const uint8_t* cache_dev,
+                                     const int32_t* topk_dev, const int32_t* block_table_dev,
+                                     const int32_t* kv_act_seqs_dev, void* out_dev, int B, int s1, int nq,
+                                     int topk, int block_size, int max_blocks_per_seq, int num_blocks,
+                                     float softmax_scale, int s2_tile, void* workspace_dev,
+                                     size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q_nope_dev || !q_rope_dev || !cache_dev || !topk_dev || !block_table_dev || !kv_act_seqs_dev ||
+        !out_dev)
+        return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
+    size_t need = 0;
+    pa_status_t st = pa_fp8_mla_workspace_size(B, s1, nq, topk, s2_tile, &need);
+    if (st != PA_OK) return st;
+    if (block_size != pa::kBlock)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (only 128)", block_size);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID, "max_blocks_per_seq (%d) and num_blocks (%d) must be positive",
+                    max_blocks_per_seq, num_blocks);
+    if ((int64_t)num_blocks * block_size > ((int64_t)1 << 31) - 1)
+        return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size exceeds 2^31 - 1 rows");
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size exceeds 2^30 tokens");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+        return fail(PA_ERR_INVALID, "softmax_scale must be finite and > 0");
+    if (!workspace_dev || workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace_dev ? workspace_bytes : (size_t)0);
+    pa::MlaParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q_nope = static_cast<const uint16_t*>(q_nope_dev);
+    p.q_rope = static_cast<const uint16_t*>(q_rope_dev);
+    p.cache = cache_dev;
+    p.topk_idx = topk_dev;
+    p.block_table = block_table_dev;
+    p.seqs = kv_act_seqs_dev;
+    p.out = static_cast<uint16_t*>(out_dev);
+    const size_t rows = (size_t)B * s1 * nq;
+    p.ntiles_max = (topk + s2_tile - 1) / s2_tile;
+    char* base = static_cast<char*>(workspace_dev);
+    p.part_ml = reinterpret_cast<float*>(base);
+    p.part_o = reinterpret_cast<float*>(base + align256(rows * p.ntiles_max * 2 * sizeof(float)));
+    p.B = B;
+    p.s1 = s1;
+    p.nq = nq;
+    p.topk = topk;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.capacity = max_blocks_per_seq * block_size;
+    p.s2_tile = s2_tile;
+    p.softmax_scale = softmax_scale;
+    hipError_t e = pa::launch_mla(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 const char* pa_fp8_last_error(void) { return g_err; }
 
 const char* pa_fp8_version(void) { return "pa_fp8 0.1 gfx950"; }

@@ -33,7 +33,24 @@ struct DecodeParams {
     float softmax_scale;
 };
 
+// MLA-style sparse decode (one latent KV head, 672-byte cache rows).
+struct MlaParams {
+    const uint16_t* q_nope;     // [B*s1*nq, 512] bf16
+    const uint16_t* q_rope;     // [B*s1*nq, 64] bf16
+    const uint8_t* cache;       // [num_blocks*128, 672] bytes
+    const int32_t* topk_idx;    // [B*s1, topk] logical token positions
+    const int32_t* block_table; // [B, max_blocks]
+    const int32_t* seqs;        // [B]
+    uint16_t* out;              // [B*s1*nq, 512] bf16
+    float* part_o;              // [B*s1*nq, ntiles_max, 512]
+    float* part_ml;             // [B*s1*nq, ntiles_max, 2]  (tile max in log2 units, sum)
+    int B, s1, nq, topk, max_blocks, num_blocks, capacity, s2_tile, ntiles_max;
+    float softmax_scale;
+};
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, bool debug);
+bool mla_supported(int nq, int s2_tile);
+hipError_t launch_mla(const MlaParams& p, hipStream_t stream);
 int grid_size(const DecodeParams& p);
 bool rows_path_supported(int nkv, int s2_tile, int rows, int s1, int nq, int B);
 hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t stream, bool debug);

@@ -1,0 +1,311 @@
+// MLA-style sparse attention decode with an FP8 latent cache (MI355X / gfx950).
+//
+// Web page "PyPTO-Gym 算子实战DeepSeek V32 MLA 的 Sparse Attention FP8 反量化算子":
+// a cache row is 672 bytes -- 512 E4M3 "nope" values, 64 BF16 "rope" values
+// (bytes 512..639) and four FP32 scales, one per 128-value group (bytes
+// 640..655) -- section 核心参数与 KV Cache 布局.  Per query token, the first
+// n = clamp(seq - s1 + 1 + s, 0, topk) top-k indices name logical tokens; each
+// is mapped through the block table to a row (section 关键实现细节), dequantised
+// to BF16 (value x group scale in FP32, then BF16), K = [nope | rope] and
+// V = nope (section 计算流程).  Per tile of s2_tile indices: S = [qn | qr] . K
+// x softmax_scale, m = tile max, P = exp(S - m) in BF16 feeds P.V while the
+// unquantised P feeds the running sum; tiles are merged online and the result
+// divided by the sum (section 在线反量化与 Online Softmax).
+//
+// Work: one workgroup per (query token, tile, block of 32 query heads); four
+// waves.  Wave w computes the scores of rows [w T/4, (w+1) T/4) of the tile for
+// the 32 heads, gathering and dequantising K straight into MFMA operands
+// (16x16x32 bf16, products exact, FP32 accumulation).  The waves exchange row
+// maxima and sums through LDS and publish BF16 P in LDS; then wave w computes
+// P.V for output channels [128 w, 128 w + 128) over all rows of the tile,
+// dequantising V rows on the fly (an 8x8 byte transpose turns row-major codes
+// into MFMA operands).  Each (token, head, tile) leaves an (O, m, l) partial;
+// mla_merge_kernel combines the tiles of each (token, head).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_fp8_common.h"
+#include "pa_fp8_device.h"
+
+namespace pa {
+
+constexpr int kMlaNope = 512, kMlaRope = 64, kMlaRow = 672, kMlaHeads = 32;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (two dwords, byte i = value i), each times its own FP32
+// scale, rounded to BF16 (the dequantised key of the page: FP32 product, BF16).
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w0, uint32_t w1, const float* sc) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    bf16x8 r;
+    r[0] = (__bf16)(a[0] * sc[0]);
+    r[1] = (__bf16)(a[1] * sc[1]);
+    r[2] = (__bf16)(b[0] * sc[2]);
+    r[3] = (__bf16)(b[1] * sc[3]);
+    r[4] = (__bf16)(c[0] * sc[4]);
+    r[5] = (__bf16)(c[1] * sc[5]);
+    r[6] = (__bf16)(d[0] * sc[6]);
+    r[7] = (__bf16)(d[1] * sc[7]);
+    return r;
+}
+
+template <int T>
+__global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
+    constexpr int RW = T / 4;             // rows of the tile whose scores a wave computes
+    constexpr int NCH = RW / 32;          // 32-row chunks per wave
+    constexpr int NB = T / 32;            // 32-row blocks of the tile
+    static_assert(NCH >= 1, "tile of at least 128 indices");
+
+    __shared__ int s_row[T];                                   // cache row of each tile position, -1 = past n
+    __shared__ __attribute__((aligned(16))) uint8_t s_p[NB][2][64 * 16];   // BF16 P, MFMA A-operand layout
+    __shared__ float s_max[4][kMlaHeads], s_sum[4][kMlaHeads];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nhb = a.nq / kMlaHeads;
+    const int hb = blockIdx.x % nhb;
+    const int rest = blockIdx.x / nhb;
+    const int t = rest % a.ntiles_max, bs = rest / a.ntiles_max;
+    const int b = bs / a.s1, s = bs - b * a.s1;
+
+    int seq = a.seqs[b];
+    seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
+    int n = seq - a.s1 + 1 + s;
+    n = n < 0 ? 0 : (n > a.topk ? a.topk : n);
+    if (t * T >= n) return;                                    // no such tile for this token
+
+    // ---- cache rows of the tile's positions -----------------------------------------------
+    for (int i = threadIdx.x; i < T; i += 256) {
+        const int j = t * T + i;
+        int row = -1;
+        if (j < n) {
+            int pos = a.topk_idx[(int64_t)bs * a.topk + j];
+            pos = pos < 0 ? 0 : (pos >= seq ? seq - 1 : pos);
+            int id = a.block_table[(int64_t)b * a.max_blocks + pos / kBlock];
+            id = (id < 0 || id >= a.num_blocks) ? 0 : id;
+            row = id * kBlock + pos % kBlock;
+        }
+        s_row[i] = row;
+    }
+
+    // ---- query operands: heads h0 + 16 hh + lr; k-slot order shared with K ----------------
+    // MFMA ks (0..15) takes nope channels 64 (ks / 2) + 16 g + 8 (ks % 2) + [0, 8);
+    // ks 16, 17 take rope channels 16 g + 8 (ks - 16) + [0, 8).
+    const int h0 = hb * kMlaHeads;
+    bf16x8 qop[2][18];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int64_t qrow = (int64_t)bs * a.nq + h0 + 16 * hh + lr;
+        const uint16_t* qn = a.q_nope + qrow * kMlaNope;
+        const uint16_t* qr = a.q_rope + qrow * kMlaRope;
+#pragma unroll
+        for (int pr = 0; pr < 8; ++pr) {
+            const i32x4 x0 = *reinterpret_cast<const i32x4*>(qn + 64 * pr + 16 * lg);
+            const i32x4 x1 = *reinterpret_cast<const i32x4*>(qn + 64 * pr + 16 * lg + 8);
+            qop[hh][2 * pr] = __builtin_bit_cast(bf16x8, x0);
+            qop[hh][2 * pr + 1] = __builtin_bit_cast(bf16x8, x1);
+        }
+        const i32x4 r0 = *reinterpret_cast<const i32x4*>(qr + 16 * lg);
+        const i32x4 r1 = *reinterpret_cast<const i32x4*>(qr + 16 * lg + 8);
+        qop[hh][16] = __builtin_bit_cast(bf16x8, r0);
+        qop[hh][17] = __builtin_bit_cast(bf16x8, r1);
+    }
+    __syncthreads();
+
+    // ---- scores of this wave's rows: S^T (rows x heads), log2 units ------------------------
+    const float coef = a.softmax_scale * kLog2e;
+    float sv[2][NCH][8];
+    float rmax[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int li = w * RW + 32 * c + 16 * k + lr;     // this lane's K row (A operand row lr)
+            const int row = s_row[li];
+            const uint8_t* rp = a.cache + (int64_t)(row < 0 ? 0 : row) * kMlaRow;
+            const f32x4 gs = *reinterpret_cast<const f32x4*>(rp + 640);
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int pr = 0; pr < 8; ++pr) {
+                const i32x4 x = *reinterpret_cast<const i32x4*>(rp + 64 * pr + 16 * lg);
+                const float g = gs[pr >> 1];
+                const float sc[8] = {g, g, g, g, g, g, g, g};
+                const bf16x8 k0 = dequant8((uint32_t)x[0], (uint32_t)x[1], sc);
+                const bf16x8 k1 = dequant8((uint32_t)x[2], (uint32_t)x[3], sc);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    acc[hh] = mfma_bf16(k0, qop[hh][2 * pr], acc[hh]);
+                    acc[hh] = mfma_bf16(k1, qop[hh][2 * pr + 1], acc[hh]);
+                }
+            }
+            const i32x4 r0 = *reinterpret_cast<const i32x4*>(rp + kMlaNope + 32 * lg);
+            const i32x4 r1 = *reinterpret_cast<const i32x4*>(rp + kMlaNope + 32 * lg + 16);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                acc[hh] = mfma_bf16(__builtin_bit_cast(bf16x8, r0), qop[hh][16], acc[hh]);
+                acc[hh] = mfma_bf16(__builtin_bit_cast(bf16x8, r1), qop[hh][17], acc[hh]);
+            }
+            // lane (head lr, group lg) holds rows 16 k + 4 lg + i of this 32-row chunk
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = s_row[w * RW + 32 * c + 16 * k + 4 * lg + i] >= 0;
+                    const float x = ok ? acc[hh][i] * coef : -INFINITY;
+                    sv[hh][c][4 * k + i] = x;
+                    rmax[hh] = fmaxf(rmax[hh], x);
+                }
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const float m = wave_max_over_groups(rmax[hh]);
+        if (lg == 0) s_max[w][16 * hh + lr] = m;
+    }
+    __syncthreads();
+
+    // ---- tile max, P = exp2(S - m) in BF16 to LDS, unquantised sums -------------------------
+    float mt[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int hc = 16 * hh + lr;
+        mt[hh] = fmaxf(fmaxf(s_max[0][hc], s_max[1][hc]), fmaxf(s_max[2][hc], s_max[3][hc]));
+        float l = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            bf16x8 pb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float pv = __builtin_amdgcn_exp2f(sv[hh][c][j] - mt[hh]);
+                l += pv;
+                pb[j] = (__bf16)pv;
+            }
+            *reinterpret_cast<bf16x8*>(&s_p[w * NCH + c][hh][16 * lane]) = pb;
+        }
+        l = wave_sum_over_groups(l);
+        if (lg == 0) s_sum[w][hc] = l;
+    }
+    __syncthreads();
+
+    // ---- P.V for channels [128 w, 128 w + 128): O[head][channel] -------------------------
+    f32x4 O[2][8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) O[hh][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bi = 0; bi < NB; ++bi) {
+        bf16x8 pop[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) pop[hh] = *reinterpret_cast<const bf16x8*>(&s_p[bi][hh][16 * lane]);
+        uint32_t xl[8], xh[8];
+        float scj[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = s_row[32 * bi + chunk_token(lg, j)];
+            const uint8_t* rp = a.cache + (int64_t)(row < 0 ? 0 : row) * kMlaRow;
+            const uint2 x = *reinterpret_cast<const uint2*>(rp + 128 * w + 8 * lr);
+            const float g = *reinterpret_cast<const float*>(rp + 640 + 4 * w);
+            xl[j] = row < 0 ? 0u : x.x;            // positions past n: zero codes (P is 0 there)
+            xh[j] = row < 0 ? 0u : x.y;
+            scj[j] = g;
+        }
+        uint32_t ylo[8], yhi[8];
+        transpose4(xl[0], xl[1], xl[2], xl[3], ylo[0], ylo[1], ylo[2], ylo[3]);
+        transpose4(xl[4], xl[5], xl[6], xl[7], yhi[0], yhi[1], yhi[2], yhi[3]);
+        transpose4(xh[0], xh[1], xh[2], xh[3], ylo[4], ylo[5], ylo[6], ylo[7]);
+        transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const bf16x8 vop = dequant8(ylo[c], yhi[c], scj);      // channel 128 w + 8 lr + c, 8 rows
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) O[hh][c] = mfma_bf16(pop[hh], vop, O[hh][c]);
+        }
+    }
+
+    // ---- partial of this tile: O (relative to the tile max), m, l --------------------------
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int head = h0 + 16 * hh + 4 * lg + i;
+            const int64_t slot = ((int64_t)bs * a.nq + head) * a.ntiles_max + t;
+            float* po = a.part_o + slot * kMlaNope + 128 * w + 8 * lr;
+            *reinterpret_cast<f32x4*>(po) = f32x4{O[hh][0][i], O[hh][1][i], O[hh][2][i], O[hh][3][i]};
+            *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[hh][4][i], O[hh][5][i], O[hh][6][i], O[hh][7][i]};
+        }
+        if (w == 0 && lg == 0) {
+            const int hc = 16 * hh + lr;
+            const int64_t slot = ((int64_t)bs * a.nq + h0 + hc) * a.ntiles_max + t;
+            a.part_ml[slot * 2] = mt[hh];
+            a.part_ml[slot * 2 + 1] = s_sum[0][hc] + s_sum[1][hc] + s_sum[2][hc] + s_sum[3][hc];
+        }
+    }
+}
+
+// Online merge of the tile partials of every (query token, head), in tile order;
+// one wave per (token, head), eight channels per lane.  n == 0 gives zeros.
+__global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams a, int T) {
+    const int lane = threadIdx.x & 63;
+    const int64_t qh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);      // (token, head)
+    if (qh >= (int64_t)a.B * a.s1 * a.nq) return;
+    const int bs = (int)(qh / a.nq);
+    const int b = bs / a.s1, s = bs - b * a.s1;
+    int seq = a.seqs[b];
+    seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
+    int n = seq - a.s1 + 1 + s;
+    n = n < 0 ? 0 : (n > a.topk ? a.topk : n);
+    const int nt = (n + T - 1) / T;
+    float M = -INFINITY, L = 0.f;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < nt; ++t) {
+        const int64_t slot = qh * a.ntiles_max + t;
+        const float m = a.part_ml[slot * 2], l = a.part_ml[slot * 2 + 1];
+        const float* po = a.part_o + slot * kMlaNope + 8 * lane;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+        const float mn = fmaxf(M, m);
+        const float fa = __builtin_amdgcn_exp2f(M - mn), fb = __builtin_amdgcn_exp2f(m - mn);
+        L = L * fa + l * fb;
+        o0 = o0 * fa + x0 * fb;
+        o1 = o1 * fa + x1 * fb;
+        M = mn;
+    }
+    const float inv = nt > 0 ? 1.f / L : 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float y0 = (c < 2 ? o0[2 * c] : o1[2 * c - 4]) * inv;
+        const float y1 = (c < 2 ? o0[2 * c + 1] : o1[2 * c - 3]) * inv;
+        pk[c] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+    }
+    *reinterpret_cast<i32x4*>(a.out + qh * kMlaNope + 8 * lane) = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+}
+
+template <int T>
+static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
+    const int64_t grid = (int64_t)p.B * p.s1 * p.ntiles_max * (p.nq / kMlaHeads);
+    if (grid > 0) hipLaunchKernelGGL((mla_decode_kernel<T>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)p.B * p.s1 * p.nq;
+    hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, p, T);
+    return hipGetLastError();
+}
+
+bool mla_supported(int nq, int s2_tile) {
+    return nq % kMlaHeads == 0 && (s2_tile == 128 || s2_tile == 256 || s2_tile == 512);
+}
+
+hipError_t launch_mla(const MlaParams& p, hipStream_t st) {
+    switch (p.s2_tile) {
+        case 128: return launch_mla_t<128>(p, st);
+        case 256: return launch_mla_t<256>(p, st);
+        default: return launch_mla_t<512>(p, st);
+    }
+}
+
+}  // namespace pa

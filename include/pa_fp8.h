@@ -129,6 +129,41 @@ pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev,
                                 int num_splits, void* workspace_dev, size_t workspace_bytes,
                                 int32_t* rows_dev, uint8_t* q8_dev, void* stream);
 
+/*
+ * Workspace bytes pa_fp8_mla_sparse_decode needs for these sizes.
+ */
+pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_tile, size_t* bytes_host);
+
+/*
+ * MLA-style sparse attention decode over an FP8 latent cache, [P2] sections
+ * 核心参数与 KV Cache 布局, 计算流程, 关键实现细节 and 在线反量化与 Online Softmax.
+ * One latent KV head shared by all nq query heads.  For batch b and query
+ * position s < s1, the first n = clamp(seq_b - s1 + 1 + s, 0, topk) entries
+ * of topk_dev[b*s1 + s] are logical token positions (clamped to [0, seq_b));
+ * position p reads cache row block_table[b, p / 128] * 128 + p % 128.
+ *   kn[c] = bf16(fp32(e4m3(row[c]) * scale[c / 128]))   c < 512 (row bytes 0..511,
+ *           scales = FP32 at bytes 640..655)
+ *   kr    = the 64 BF16 values at row bytes 512..639;  K = [kn | kr], V = kn
+ *   per tile of s2_tile positions: S = [qn | qr] . K * softmax_scale,
+ *   m = max S, P = exp(S - m); bf16(P) . V and the unquantised sum of P are
+ *   merged over tiles; out = bf16(O / L).  n == 0 gives zero rows.
+ * Layouts:
+ *   q_nope_dev   [B*s1*nq, 512] bf16      q_rope_dev [B*s1*nq, 64] bf16
+ *   cache_dev    [num_blocks*128, 672] bytes (one row per token slot)
+ *   topk_dev     [B*s1, topk] int32       block_table_dev [B, max_blocks_per_seq] int32
+ *   kv_act_seqs_dev [B] int32             out_dev [B*s1*nq, 512] bf16 (written completely)
+ * Device-side rules as for pa_fp8_decode (ids < 0 or >= num_blocks read block
+ * 0; seq clamped to the table capacity).  Supported: block_size 128, nq a
+ * multiple of 32, s2_tile 128 / 256 / 512.  The workspace (size from
+ * pa_fp8_mla_workspace_size) holds per-tile partial results.
+ */
+pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_dev, const uint8_t* cache_dev,
+                                     const int32_t* topk_dev, const int32_t* block_table_dev,
+                                     const int32_t* kv_act_seqs_dev, void* out_dev, int B, int s1, int nq,
+                                     int topk, int block_size, int max_blocks_per_seq, int num_blocks,
+                                     float softmax_scale, int s2_tile, void* workspace_dev,
+                                     size_t workspace_bytes, void* stream);
+
 /* Message of the last failed call on this host thread ("" if none). */
 const char* pa_fp8_last_error(void);
 
