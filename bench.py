@@ -40,7 +40,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA)")
+    ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
     ap.add_argument("--splits", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled by the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,6 +142,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     binding.lib()
+    if args.config == 4:
+        return run_mla(args)
     cfg = synth.CONFIGS[args.config]
     sets, seqs = make_sets(cfg, max(1, args.rotate))
     nbytes = synth.gqa_algorithmic_bytes(cfg, seqs)
@@ -220,6 +222,54 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, sets, seqs, args.cpu_target_s)
+    print(json.dumps(line), flush=True)
+
+
+def run_mla(args):
+    """The MLA-style sparse decode workload (B=16, nq=128, topk 2048, seq 4k-32k)."""
+    import torch
+    from fp8_paged_kv_amd import binding, synth
+    cfg = synth.CONFIGS[4]
+    first = synth.make_mla_inputs(cfg, device="cuda")
+    seqs = first["kv_act_seqs"].cpu().tolist()
+    sets = [first] + [synth.make_mla_inputs(cfg, device="cuda", seed=1000 + 17 * i + cfg.seed, seq_lens=seqs)
+                      for i in range(1, max(1, args.rotate))]
+    out = torch.empty((cfg.B * cfg.s1 * cfg.nq, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(binding.mla_workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        binding.mla_decode_inputs(sets[i % len(sets)], out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        binding.mla_decode_inputs(sets[i % len(sets)], out=out, workspace=ws, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    nbytes = synth.mla_algorithmic_bytes(cfg, seqs)
+    ntok = sum(cfg.s1 * min(int(q), cfg.topk) for q in seqs)
+    flops = 2 * (576 + 512) * cfg.nq * ntok              # S = [qn|qr].K and P.V, per query head
+    ms = wall / args.steps * 1e3
+    mean = sum(ev) / len(ev)
+    line = {
+        "metric": "MLA sparse decode, algorithmic GB/s and bf16 TFLOP/s",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 MFMA on dequantised fp8 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "s1": cfg.s1, "nq": cfg.nq, "topk": cfg.topk,
+                   "s2_tile": cfg.s2_tile, "algorithmic_bytes_per_call": nbytes, "flop_per_call": flops},
+        "event_us_per_call": {"mean": round(mean * 1e3, 2), "median": round(ev[len(ev) // 2] * 1e3, 2)},
+        "tflop_s": round(flops / (mean * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (mean * 1e-3) / 1e12, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(flops / (mean * 1e-3) / 1e12 / 2500.0, 4), "traffic": None,
+                     "hbm_gb_s": round(nbytes / (mean * 1e-3) / 1e9, 1),
+                     "kernel": "pa::mla_decode_kernel + pa::mla_merge_kernel"},
+    }
     print(json.dumps(line), flush=True)
 
 
