@@ -95,25 +95,28 @@ bool use_rows_path(int B, int s1, int nq, int nkv, int s2_tile, int num_splits) 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
-    size_t counters, part_ml, part_o, total;
+    size_t meta, part_ml, part_o, total;   // meta: arrival counters (per-head path) or the partition (whole-row path)
 };
 
 // Per-head path with splits: [B*nkv int32 counters | pad][B*nkv*nsplit*R*2 | pad][B*nkv*nsplit*R*128]
-// Whole-row path:             [B*nkv+2 int32 partition| pad][B*nkv*KMAX*R*2 | pad][B*nkv*KMAX*R*128]
+// Whole-row path:             [B*nkv int32, untouched | pad][B*nkv+2 int32 partition | pad]
+//                             [B*nkv*KMAX*R*2 | pad][B*nkv*KMAX*R*128]
 // with KMAX = tiles per sequence at full capacity (a (batch, head) is split at most that often).
+// The whole-row path never writes the first B*nkv words, so the per-head path's arrival
+// counters stay zero when one workspace serves calls of both paths.
 WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit, bool rows, int kmax) {
     WorkspaceLayout l = {0, 0, 0, 0};
     if (rows) {
         const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
-        l.counters = 0;
-        l.part_ml = align256(((size_t)B * nkv + 2) * sizeof(int32_t));
+        l.meta = align256(units * sizeof(int32_t));
+        l.part_ml = l.meta + align256(((size_t)B * nkv + 2) * sizeof(int32_t));
         l.part_o = l.part_ml + align256(units * kmax * R * 2 * sizeof(float));
         l.total = l.part_o + units * kmax * R * pa::kHeadDim * sizeof(float);
         return l;
     }
     if (nsplit <= 1) return l;
     const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
-    l.counters = 0;
+    l.meta = 0;
     l.part_ml = align256(units * sizeof(int32_t));
     l.part_o = l.part_ml + align256(units * nsplit * R * 2 * sizeof(float));
     l.total = l.part_o + units * nsplit * R * pa::kHeadDim * sizeof(float);
@@ -165,9 +168,9 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     if (need > 0) {
         char* base = static_cast<char*>(workspace);
         if (rows)
-            p.rows_meta = reinterpret_cast<int32_t*>(base + lay.counters);
+            p.rows_meta = reinterpret_cast<int32_t*>(base + lay.meta);
         else
-            p.counters = reinterpret_cast<int32_t*>(base + lay.counters);
+            p.counters = reinterpret_cast<int32_t*>(base + lay.meta);
         p.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
         p.part_o = reinterpret_cast<float*>(base + lay.part_o);
     }

@@ -22,6 +22,10 @@ Sources for the layouts and scale rules used to *prepare* inputs:
      反量化算子" (www.mhpn.cn/news/2272720), section "核心参数与 KV Cache 布局":
      the 672-byte cache row [0:512) e4m3 nope, [512:640) 64 bf16 rope,
      [640:656) four fp32 group scales, 16 bytes of padding.
+[P5] the web page on ops-transformer's scatter_pa_kv_cache_with_k_scale
+     (www.lmnt.cn/news/278797), section 函数原型: key / value
+     [num_tokens, num_head, head_size] FP8, key_scale [num_tokens, num_head]
+     float, slot_mapping [num_tokens] int32 / int64 with distinct values.
 """
 from __future__ import annotations
 
@@ -345,3 +349,85 @@ def mla_algorithmic_bytes(cfg: MlaConfig, seqs: Sequence[int]) -> int:
         n += cfg.s1 * min(int(s), cfg.topk)
     rows = cfg.B * cfg.s1 * cfg.nq
     return n * (656 + 4 + 4) + rows * (MLA_NOPE + MLA_ROPE) * 2 + rows * MLA_NOPE * 2 + 4 * cfg.B
+
+
+# ------------------------------------------------------------ cache writer
+
+@dataclass(frozen=True)
+class ScatterConfig:
+    """Shape recipe of one call of the FP8 KV-cache writer ([P5])."""
+    name: str
+    num_tokens: int
+    num_head: int
+    k_head_size: int = 128
+    v_head_size: int = 128
+    num_blocks: int = 4
+    block_size: int = BLOCK_SIZE
+    layout: str = "BSND"          # BSND [nb, bs, H, d] (the decode's) or BNBD [nb, H, bs, d]
+    slot_bits: int = 32
+    skip: int = 0                 # tokens given a slot outside [0, num_blocks * block_size)
+    seed: int = 0
+
+
+def _random_codes(shape, g, device) -> torch.Tensor:
+    """Uniform e4m3 codes without the two NaN codes (0x7F, 0xFF)."""
+    c = torch.randint(0, 254, shape, generator=g, device=device, dtype=torch.int32)
+    c = c + (c >= 0x7F).to(torch.int32)          # skip 0x7F; 0xFF is out of range already
+    return c.to(torch.uint8)
+
+
+def make_scatter_inputs(cfg: ScatterConfig, device="cpu", seed: Optional[int] = None) -> dict:
+    """Draw one seeded writer call.
+
+    Slots are distinct: the first num_tokens entries of a random permutation
+    of the pool's slots.  ``skip`` randomly chosen tokens get a slot outside
+    the pool instead (alternately -1 - k and num_slots + k - 1).  Keys and values
+    are uniform e4m3 codes, key scales uniform in [1e-3, 1e-1), and the caches
+    start filled with random bytes / values so that untouched positions are
+    visible."""
+    seed = cfg.seed if seed is None else seed
+    g = _gen(device, seed)
+    T, H, nb, bs = cfg.num_tokens, cfg.num_head, cfg.num_blocks, cfg.block_size
+    nslots = nb * bs
+    assert T <= nslots, "more tokens than cache slots"
+    slots = torch.randperm(nslots, generator=g, device=device)[:T].to(torch.int64)
+    if cfg.skip:
+        which = torch.randperm(T, generator=g, device=device)[: cfg.skip]
+        k = torch.arange(cfg.skip, device=device, dtype=torch.int64)
+        slots[which] = torch.where(k % 2 == 0, -1 - k, nslots + k - 1)
+    slots = slots.to(torch.int32 if cfg.slot_bits == 32 else torch.int64)
+    key = _random_codes((T, H, cfg.k_head_size), g, device)
+    value = _random_codes((T, H, cfg.v_head_size), g, device)
+    key_scale = torch.rand((T, H), generator=g, device=device) * 0.099 + 0.001
+    if cfg.layout == "BSND":
+        kshape, vshape, sshape = (nb, bs, H, cfg.k_head_size), (nb, bs, H, cfg.v_head_size), (nb, bs, H)
+    else:
+        kshape, vshape, sshape = (nb, H, bs, cfg.k_head_size), (nb, H, bs, cfg.v_head_size), (nb, H, bs)
+    key_cache = _random_codes(kshape, g, device)
+    value_cache = _random_codes(vshape, g, device)
+    key_scale_cache = torch.rand(sshape, generator=g, device=device)
+    return dict(cfg=cfg, key=key, value=value, slot_mapping=slots, key_scale=key_scale,
+                key_cache=key_cache, value_cache=value_cache, key_scale_cache=key_scale_cache)
+
+
+def prefill_slots(cfg: GqaConfig, device="cpu", seed: Optional[int] = None) -> dict:
+    """Slot mapping that writes every valid token of a GQA workload's sequences.
+
+    Lengths and block table are drawn exactly as make_gqa_inputs draws them
+    (same seed, same generator order), so writing per-token rows at these
+    slots fills the pool positions the decode of that workload reads.  Token
+    order is (batch, position); slot = table[b, p // 128] * 128 + p % 128."""
+    seed = cfg.seed if seed is None else seed
+    g = _gen(device, seed)
+    seqs = _draw_seq_lens(cfg, g, device)
+    table, _, need = _block_table(cfg, seqs, g, device, False)
+    bs = cfg.block_size
+    parts = []
+    for b in range(cfg.B):
+        n = int(seqs[b])
+        if n == 0:
+            continue
+        p = torch.arange(n, dtype=torch.int64)
+        parts.append(table[b, p // bs].to(torch.int64) * bs + p % bs)
+    slots = torch.cat(parts) if parts else torch.zeros(0, dtype=torch.int64)
+    return dict(slots=slots.to(torch.int32).to(device), seqs=seqs, block_table=table)

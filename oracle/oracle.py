@@ -55,6 +55,8 @@ def lib():
         L.oracle_pa_fp8_decode_rows.restype = I
         L.oracle_mla_sparse_decode.argtypes = [P] * 6 + [I] * 7 + [ctypes.c_double] + [I] * 3 + [P] * 2
         L.oracle_mla_sparse_decode.restype = I
+        L.oracle_scatter_kv_cache.argtypes = [P] * 7 + [I] * 7 + [ctypes.c_int64] * 4
+        L.oracle_scatter_kv_cache.restype = I
         _lib = L
     return _lib
 
@@ -208,3 +210,45 @@ def mla_decode(inp, threads: int = None, b_range=None) -> dict:
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(run, [(b, b + 1) for b in range(lo, hi)]))
     return dict(out=out, out_bf16=out_bf, threads=threads)
+
+
+def scatter_kv_cache(key, value, key_cache, value_cache, slot_mapping, key_scale, key_scale_cache,
+                     layout: str = "BSND") -> dict:
+    """The [P5] cache writer on copies of the given caches.
+
+    ``key`` [T, H, dk] and ``value`` [T, H, dv] hold e4m3 codes (uint8 or
+    float8 tensors / arrays), ``key_scale`` [T, H] float32 (any strides),
+    ``slot_mapping`` [T] int32 or int64.  Caches: BSND ``[nb, bs, H, d]`` with
+    scales ``[nb, bs, H]``, or BNBD ``[nb, H, bs, d]`` with scales
+    ``[nb, H, bs]`` (a trailing axis of 1 is accepted).  Returns the updated
+    copies and the number of tokens written.
+    """
+    k = _np(key, np.uint8)
+    v = _np(value, np.uint8)
+    kc = _np(key_cache, np.uint8).copy()
+    vc = _np(value_cache, np.uint8).copy()
+    slots = np.ascontiguousarray(_slots64(slot_mapping))
+    ks = _np(key_scale, np.float32)
+    ksc = _np(key_scale_cache, np.float32).copy()
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    lay = {"BSND": 0, "BNBD": 1}[layout]
+    if lay == 0:
+        nb, bs = kc.shape[0], kc.shape[1]
+    else:
+        nb, bs = kc.shape[0], kc.shape[2]
+    n = lib().oracle_scatter_kv_cache(_ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(slots), _ptr(ks), _ptr(ksc),
+                                      T, H, dk, dv, nb, bs, lay, H * dk, H * dv, H, 1)
+    if n < 0:
+        raise ValueError("oracle_scatter_kv_cache rejected its arguments")
+    return dict(key_cache=kc, value_cache=vc, key_scale_cache=ksc, written=n)
+
+
+def _slots64(slot_mapping) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(slot_mapping, torch.Tensor):
+            return slot_mapping.detach().cpu().to(torch.int64).numpy()
+    except ImportError:
+        pass
+    return np.asarray(slot_mapping).astype(np.int64)

@@ -20,6 +20,14 @@
  *        reciprocal;
  *      - section 关键特性 (key features): E4M3 range [-448, 448], FP32
  *        softmax state.
+ * [P5] web page on ops-transformer's scatter_pa_kv_cache_with_k_scale
+ *      (www.lmnt.cn/news/278797).
+ *      - section 功能说明与计算公式: per token i and head j, block = slot / block_size,
+ *        offset = slot % block_size; the key, value and key-scale rows of (i, j)
+ *        go to that (block, head, offset) of the three caches, in place;
+ *      - section 约束说明 and the SIMT kernel paragraph: slots below 0 or above
+ *        num_blocks * block_size - 1 are skipped; repeated slots are the
+ *        caller's error (no result is promised).
  * [P2] web page "PyPTO-Gym 算子实战DeepSeek V32 MLA 的 Sparse Attention FP8 反量化
  *      算子" (www.mhpn.cn/news/2272720).
  *      - section 核心参数与 KV Cache 布局: 672-byte row = 512 e4m3 nope,
@@ -53,6 +61,11 @@
  *        code = E4M3(fp32(P / ps)); the running sum uses unquantised P.
  *  R-g   query head qh = h * G + g serves KV head h (contiguous groups).
  *  R-s1  every one of the s1 query positions attends to all of [0, seq).
+ *  R-lay the cache writer serves two layouts: BSND [block, offset, head, d]
+ *        with scales [block, offset, head] -- [P1]'s layout, the one the
+ *        decode reads -- and BNBD [block, head, offset, d] with scales
+ *        [block, head, offset] -- [P5]'s documented layout.
+ *  R-dup with a repeated slot the later token wins here (tests never repeat).
  */
 #include <math.h>
 #include <stdint.h>
@@ -495,4 +508,60 @@ int oracle_mla_sparse_decode(const uint16_t* q_nope, const uint16_t* q_rope,
     }
     free(K); free(S); free(P); free(O); free(Ot); free(qv);
     return 0;
+}
+
+/* ------------------------------------------------- [P5] FP8 KV-cache writer */
+
+/*
+ * In-place scatter of one step's FP8 key / value rows and per-(token, head)
+ * key scales into the paged caches ([P5] 功能说明与计算公式).
+ *   key   token i, head j, byte d at key[i * key_token_stride + j * k_head_size + d]
+ *   value likewise with value_token_stride and v_head_size
+ *   key_scale (i, j) at key_scale[i * ks_token_stride + j * ks_head_stride]
+ *   slots [num_tokens] (int64 here; the caller widens int32 slots)
+ * layout 0 (BSND): key_cache[((block * block_size + offset) * num_head + j) * k_head_size + d],
+ *                  key_scale_cache[(block * block_size + offset) * num_head + j];
+ * layout 1 (BNBD): key_cache[((block * num_head + j) * block_size + offset) * k_head_size + d],
+ *                  key_scale_cache[(block * num_head + j) * block_size + offset].
+ * Tokens whose slot lies outside [0, num_blocks * block_size) are skipped.
+ * Returns the number of tokens written, or -1 on a bad argument.
+ */
+int oracle_scatter_kv_cache(const uint8_t* key, const uint8_t* value,
+                            uint8_t* key_cache, uint8_t* value_cache,
+                            const int64_t* slots, const float* key_scale, float* key_scale_cache,
+                            int num_tokens, int num_head, int k_head_size, int v_head_size,
+                            int num_blocks, int block_size, int layout,
+                            int64_t key_token_stride, int64_t value_token_stride,
+                            int64_t ks_token_stride, int64_t ks_head_stride)
+{
+    if (num_tokens < 0 || num_head <= 0 || k_head_size <= 0 || v_head_size <= 0 ||
+        num_blocks <= 0 || block_size <= 0 || (layout != 0 && layout != 1))
+        return -1;
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    int written = 0;
+    for (int i = 0; i < num_tokens; ++i) {
+        const int64_t slot = slots[i];
+        if (slot < 0 || slot > num_slots - 1)
+            continue;
+        const int64_t block = slot / block_size, offset = slot % block_size;
+        for (int j = 0; j < num_head; ++j) {
+            int64_t kpos, vpos, spos;
+            if (layout == 0) {
+                kpos = ((block * block_size + offset) * num_head + j) * k_head_size;
+                vpos = ((block * block_size + offset) * num_head + j) * v_head_size;
+                spos = (block * block_size + offset) * num_head + j;
+            } else {
+                kpos = ((block * num_head + j) * block_size + offset) * k_head_size;
+                vpos = ((block * num_head + j) * block_size + offset) * v_head_size;
+                spos = (block * num_head + j) * block_size + offset;
+            }
+            for (int d = 0; d < k_head_size; ++d)
+                key_cache[kpos + d] = key[(int64_t)i * key_token_stride + (int64_t)j * k_head_size + d];
+            for (int d = 0; d < v_head_size; ++d)
+                value_cache[vpos + d] = value[(int64_t)i * value_token_stride + (int64_t)j * v_head_size + d];
+            key_scale_cache[spos] = key_scale[(int64_t)i * ks_token_stride + (int64_t)j * ks_head_stride];
+        }
+        ++written;
+    }
+    return written;
 }

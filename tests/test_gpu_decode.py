@@ -173,3 +173,21 @@ def _run_dev(B, inp_d, tag, num_splits=0):
     out = B.decode_inputs(inp_d, num_splits=num_splits)
     torch.cuda.synchronize()
     return gpu_out_float(out)
+
+
+def test_shared_workspace_between_paths(B, oracle_mod):
+    """One zero-filled workspace serving whole-row calls and split calls in turn:
+    the whole-row path must leave the split path's arrival counters at zero."""
+    cfg = _case("shared-ws", B=3, seq_lens=(1500, 700, 2100), num_blocks=60, max_blocks_per_seq=20, seed=21)
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    d = to_device(inp)
+    c = inp["cfg"]
+    need = max(B.workspace_size(c.B, c.s1, c.nq, c.nkv, c.D, 128, c.max_blocks_per_seq, c.s2_tile, ns)[0]
+               for ns in (0, 3))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, ns in enumerate((0, 3, 0, 3)):
+        print(f"[gpu] shared workspace call {i} splits={ns}", flush=True)
+        out = B.decode_inputs(d, num_splits=ns, workspace=ws)
+        torch.cuda.synchronize()
+        compare(gpu_out_float(out), ref["out_bf16"], f"shared workspace call {i} splits={ns}")
