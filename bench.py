@@ -41,6 +41,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
+    ap.add_argument("--op", choices=["decode", "scatter"], default="decode",
+                    help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write)")
     ap.add_argument("--splits", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled by the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,6 +144,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     binding.lib()
+    if args.op == "scatter":
+        return run_scatter(args)
     if args.config == 4:
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
@@ -269,6 +273,80 @@ def run_mla(args):
                      "unit": "TFLOP/s", "frac": round(flops / (mean * 1e-3) / 1e12 / 2500.0, 4), "traffic": None,
                      "hbm_gb_s": round(nbytes / (mean * 1e-3) / 1e9, 1),
                      "kernel": "pa::mla_decode_kernel + pa::mla_merge_kernel"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _time(fn, steps, warmup):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn(stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+
+
+def run_scatter(args):
+    """The FP8 KV-cache writer: every token of the GLM-4.5-shaped workload
+    (B=32, lengths U[1024, 8192], 8 KV heads, D=128) written into its
+    2048-block pool in the decode's layout, int32 slots; plus one decode step
+    (one new token per sequence)."""
+    import torch
+    from fp8_paged_kv_amd import binding, synth
+    cfg = synth.CONFIGS[1]
+    pre = synth.prefill_slots(cfg, device="cuda")
+    slots = pre["slots"]
+    T, H, D = int(slots.numel()), cfg.nkv, cfg.D
+    g = torch.Generator(device="cuda").manual_seed(7)
+    key = torch.randint(0, 256, (T, H, D), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    value = torch.randint(0, 256, (T, H, D), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    ks = torch.rand((T, H), generator=g, device="cuda")
+    shape = (cfg.num_blocks, cfg.block_size, H, D)
+    kc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    ksc = torch.zeros(shape[:3], device="cuda")
+
+    def call(stream):
+        binding.scatter_kv_cache(key, value, kc, vc, slots, ks, ksc, "BSND", stream=stream)
+
+    wall, ev = _time(call, args.steps, args.warmup)
+    per_tok = 2 * (2 * H * D + 4 * H) + 4          # read + write of both rows and the scales, the slot
+    nbytes = T * per_tok
+    # decode step: one token per sequence, at position seq_b (the next slot of each table row)
+    seqs = pre["seqs"].tolist()
+    step_slots = torch.tensor([int(pre["block_table"][b, (s - 1) // 128]) * 128 + (s - 1) % 128
+                               for b, s in enumerate(seqs)], dtype=torch.int32, device="cuda")
+    kd, vd, sd = key[: cfg.B].contiguous(), value[: cfg.B].contiguous(), ks[: cfg.B].contiguous()
+
+    def step(stream):
+        binding.scatter_kv_cache(kd, vd, kc, vc, step_slots, sd, ksc, "BSND", stream=stream)
+
+    _, ev_step = _time(step, args.steps, args.warmup)
+    ms = wall / args.steps * 1e3
+    mean = sum(ev) / len(ev)
+    achieved = nbytes / (mean * 1e-3) / 1e9
+    line = {
+        "metric": "FP8 KV-cache writer, algorithmic GB/s", "value": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8 (fp8 codes copied)",
+        "data": "synthetic",
+        "config": {"workload": "kv-writer-prefill-glm45-b32-nkv8-seq1k-8k", "num_tokens": T, "num_head": H,
+                   "head_size": D, "num_blocks": cfg.num_blocks, "block_size": cfg.block_size, "layout": "BSND",
+                   "slot_bits": 32, "algorithmic_bytes_per_call": nbytes},
+        "event_us_per_call": {"mean": round(mean * 1e3, 2), "median": round(ev[len(ev) // 2] * 1e3, 2)},
+        "decode_step_us": {"tokens": cfg.B, "median": round(ev_step[len(ev_step) // 2] * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa::scatter_kv_kernel<int, 0>"},
     }
     print(json.dumps(line), flush=True)
 

@@ -19,8 +19,10 @@ LIB_PATH = os.environ.get("PA_FP8_LIB") or os.path.join(PKG, "libpa_fp8.so")
 PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
 
 EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug",
-           "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode",
+           "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode", "pa_fp8_scatter_kv_cache",
            "pa_fp8_last_error", "pa_fp8_version")
+
+PA_CACHE_BSND, PA_CACHE_BNBD = 0, 1
 
 
 class PaError(RuntimeError):
@@ -51,6 +53,8 @@ def lib():
         L.pa_fp8_mla_workspace_size.restype = I
         L.pa_fp8_mla_sparse_decode.argtypes = [P] * 7 + [I] * 7 + [F, I, P, Z, P]
         L.pa_fp8_mla_sparse_decode.restype = I
+        L.pa_fp8_scatter_kv_cache.argtypes = [P] * 7 + [I] * 8 + [ctypes.c_int64] * 4 + [P]
+        L.pa_fp8_scatter_kv_cache.restype = I
         L.pa_fp8_last_error.argtypes = []
         L.pa_fp8_last_error.restype = ctypes.c_char_p
         L.pa_fp8_version.argtypes = []
@@ -183,3 +187,45 @@ def mla_decode_inputs(inp: dict, out=None, workspace=None, stream=None):
     return mla_decode(inp["q_nope"], inp["q_rope"], inp["cache"], inp["topk"], inp["block_table"],
                       inp["kv_act_seqs"], inp["softmax_scale"], inp.get("s2_tile", cfg.s2_tile), cfg.s1,
                       out=out, workspace=workspace, stream=stream, block_size=cfg.block_size)
+
+
+def scatter_kv_cache(key, value, key_cache, value_cache, slot_mapping, key_scale, key_scale_cache,
+                     layout: str = "BSND", stream=None):
+    """In-place FP8 KV-cache write (pa_fp8_scatter_kv_cache).
+
+    key [T, H, dk] / value [T, H, dv]: uint8 or float8_e4m3fn, rows may be
+    strided over tokens (each token's [H, d] block contiguous); key_scale
+    [T, H] float32, any strides; slot_mapping [T] int32 / int64.
+    layout "BSND": caches [nb, bs, H, d], key_scale_cache [nb, bs, H];
+    layout "BNBD": caches [nb, H, bs, d], key_scale_cache [nb, H, bs] or [nb, H, bs, 1]."""
+    T, H, dk = (int(x) for x in key.shape)
+    dv = int(value.shape[2])
+    for name, t, d in (("key", key, dk), ("value", value, dv)):
+        if t.element_size() != 1 or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name}: one-byte codes with each token's [H, d] block contiguous")
+    for name, t in (("key_cache", key_cache), ("value_cache", value_cache), ("key_scale_cache", key_scale_cache)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if key_scale.dtype != torch.float32 or key_scale_cache.dtype != torch.float32:
+        raise ValueError("key_scale and key_scale_cache must be float32")
+    if slot_mapping.dtype not in (torch.int32, torch.int64):
+        raise ValueError("slot_mapping must be int32 or int64")
+    lay = {"BSND": PA_CACHE_BSND, "BNBD": PA_CACHE_BNBD}[layout]
+    nb = int(key_cache.shape[0])
+    bs = int(key_cache.shape[1] if lay == PA_CACHE_BSND else key_cache.shape[2])
+    for name, t in (("key", key), ("value", value), ("key_scale", key_scale), ("slot_mapping", slot_mapping)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    _checked_inputs(dict(key_cache=key_cache, value_cache=value_cache, key_scale_cache=key_scale_cache,
+                         slot_mapping=slot_mapping))
+    _check(lib().pa_fp8_scatter_kv_cache(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), _ptr(key_scale),
+        _ptr(key_scale_cache), T, H, dk, dv, nb, bs, 32 if slot_mapping.dtype == torch.int32 else 64, lay,
+        key.stride(0), value.stride(0), key_scale.stride(0), key_scale.stride(1), _stream(stream)))
+
+
+def scatter_inputs(inp: dict, stream=None):
+    """scatter_kv_cache() on a dict produced by fp8_paged_kv_amd.synth.make_scatter_inputs
+    (updates the dict's caches in place)."""
+    scatter_kv_cache(inp["key"], inp["value"], inp["key_cache"], inp["value_cache"], inp["slot_mapping"],
+                     inp["key_scale"], inp["key_scale_cache"], inp["cfg"].layout, stream=stream)

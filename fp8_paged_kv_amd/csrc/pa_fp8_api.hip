@@ -320,6 +320,60 @@ pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_
     return PA_OK;
 }
 
+pa_status_t pa_fp8_scatter_kv_cache(const uint8_t* key_dev, const uint8_t* value_dev, uint8_t* key_cache_dev,
+                                    uint8_t* value_cache_dev, const void* slot_mapping_dev,
+                                    const float* key_scale_dev, float* key_scale_cache_dev, int num_tokens,
+                                    int num_head, int k_head_size, int v_head_size, int num_blocks,
+                                    int block_size, int slot_bits, int layout, int64_t key_token_stride,
+                                    int64_t value_token_stride, int64_t key_scale_token_stride,
+                                    int64_t key_scale_head_stride, void* stream) {
+    g_err[0] = 0;
+    if (!key_dev || !value_dev || !key_cache_dev || !value_cache_dev || !slot_mapping_dev || !key_scale_dev ||
+        !key_scale_cache_dev)
+        return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
+    if (num_tokens <= 0 || num_head <= 0 || k_head_size <= 0 || v_head_size <= 0 || num_blocks <= 0 ||
+        block_size <= 0)
+        return fail(PA_ERR_INVALID, "sizes must be positive (num_tokens=%d num_head=%d k_head_size=%d "
+                    "v_head_size=%d num_blocks=%d block_size=%d)", num_tokens, num_head, k_head_size,
+                    v_head_size, num_blocks, block_size);
+    if (slot_bits != 32 && slot_bits != 64) return fail(PA_ERR_INVALID, "slot_bits must be 32 or 64 (got %d)", slot_bits);
+    if (layout != PA_CACHE_BSND && layout != PA_CACHE_BNBD)
+        return fail(PA_ERR_INVALID, "layout must be PA_CACHE_BSND or PA_CACHE_BNBD (got %d)", layout);
+    if (key_token_stride < (int64_t)num_head * k_head_size || value_token_stride < (int64_t)num_head * v_head_size)
+        return fail(PA_ERR_INVALID, "token strides must cover num_head * head_size bytes");
+    if (key_scale_token_stride < 0 || key_scale_head_stride < 0)
+        return fail(PA_ERR_INVALID, "key_scale strides must be >= 0");
+    if (k_head_size % 16 || v_head_size % 16 || key_token_stride % 16 || value_token_stride % 16)
+        return fail(PA_ERR_UNSUPPORTED, "head sizes and token strides must be multiples of 16 bytes");
+    auto mis = [](const void* ptr, uintptr_t al) { return (reinterpret_cast<uintptr_t>(ptr) & (al - 1)) != 0; };
+    if (mis(key_dev, 16) || mis(value_dev, 16) || mis(key_cache_dev, 16) || mis(value_cache_dev, 16) ||
+        mis(key_scale_dev, 4) || mis(key_scale_cache_dev, 4) || mis(slot_mapping_dev, slot_bits / 8))
+        return fail(PA_ERR_UNSUPPORTED, "rows and caches must be 16-byte aligned, scales 4-byte, slots "
+                    "aligned to their width");
+    pa::ScatterParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.key = key_dev;
+    p.value = value_dev;
+    p.key_cache = key_cache_dev;
+    p.value_cache = value_cache_dev;
+    p.slots = slot_mapping_dev;
+    p.key_scale = key_scale_dev;
+    p.key_scale_cache = key_scale_cache_dev;
+    p.num_tokens = num_tokens;
+    p.num_slots = (int64_t)num_blocks * block_size;
+    p.num_head = num_head;
+    p.k_head_size = k_head_size;
+    p.v_head_size = v_head_size;
+    p.block_size = block_size;
+    p.k_stride = key_token_stride;
+    p.v_stride = value_token_stride;
+    p.ks_token_stride = key_scale_token_stride;
+    p.ks_head_stride = key_scale_head_stride;
+    hipError_t e = pa::launch_scatter_kv(p, slot_bits, layout, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 const char* pa_fp8_last_error(void) { return g_err; }
 
 const char* pa_fp8_version(void) { return "pa_fp8 0.1 gfx950"; }

@@ -48,7 +48,22 @@ struct MlaParams {
     float softmax_scale;
 };
 
+// FP8 KV-cache writer (slot scatter of key / value rows and key scales).
+struct ScatterParams {
+    const uint8_t* key;         // token i, head j at key + i * k_stride + j * k_head_size
+    const uint8_t* value;       // likewise with v_stride, v_head_size
+    uint8_t* key_cache;         // BSND [nb, bs, H, dk] or BNBD [nb, H, bs, dk]
+    uint8_t* value_cache;       // same layout with dv
+    const void* slots;          // [num_tokens] int32 or int64
+    const float* key_scale;     // (i, j) at i * ks_token_stride + j * ks_head_stride
+    float* key_scale_cache;     // BSND [nb, bs, H] or BNBD [nb, H, bs]
+    int64_t num_tokens, num_slots;
+    int num_head, k_head_size, v_head_size, block_size;
+    int64_t k_stride, v_stride, ks_token_stride, ks_head_stride;
+};
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, bool debug);
+hipError_t launch_scatter_kv(const ScatterParams& p, int slot_bits, int layout, hipStream_t stream);
 bool mla_supported(int nq, int s2_tile);
 hipError_t launch_mla(const MlaParams& p, hipStream_t stream);
 int grid_size(const DecodeParams& p);

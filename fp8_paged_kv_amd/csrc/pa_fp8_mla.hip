@@ -67,8 +67,18 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int nhb = a.nq / kMlaHeads;
-    const int hb = blockIdx.x % nhb;
-    const int rest = blockIdx.x / nhb;
+    const int nbt = (int)gridDim.x / nhb;                      // (token, tile) pairs
+    int hb, rest;
+    if (nbt % 8 == 0) {
+        // workgroups are dealt round-robin to the 8 XCDs: keep the head blocks of one
+        // (token, tile) on one XCD so its L2 serves the rows they all gather
+        const int x = (int)blockIdx.x % 8, k = (int)blockIdx.x / 8;
+        hb = k % nhb;
+        rest = x + 8 * (k / nhb);
+    } else {
+        hb = (int)blockIdx.x % nhb;
+        rest = (int)blockIdx.x / nhb;
+    }
     const int t = rest % a.ntiles_max, bs = rest / a.ntiles_max;
     const int b = bs / a.s1, s = bs - b * a.s1;
 

@@ -15,6 +15,10 @@
  *      — the two-phase convention (query the workspace size, then run with
  *      a caller-owned workspace) and distinct null-pointer / invalid-argument
  *      status codes.
+ * [P5] the ops-transformer scatter_pa_kv_cache_with_k_scale page
+ *      (www.lmnt.cn/news/278797) — the FP8 KV-cache writer: section
+ *      功能说明与计算公式 (slot -> block, offset), section 函数原型 and 约束说明
+ *      (tensors, layouts, skipped slots).
  *
  * Conventions for every entry point:
  *  - Pointers named *_dev are device pointers (HBM of the current device);
@@ -54,6 +58,12 @@ enum {
     PA_ERR_UNSUPPORTED = 3,  /* legal in principle but not built (e.g. D != 128) */
     PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required          */
     PA_ERR_HIP = 5           /* the HIP runtime reported an error at launch      */
+};
+
+/* Paged-cache layouts of the cache writer. */
+enum {
+    PA_CACHE_BSND = 0,       /* [num_blocks, block_size, num_head, head_size] — the decode's layout ([P1]) */
+    PA_CACHE_BNBD = 1        /* [num_blocks, num_head, block_size, head_size] — [P5]'s default          */
 };
 
 /*
@@ -163,6 +173,42 @@ pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_
                                      int topk, int block_size, int max_blocks_per_seq, int num_blocks,
                                      float softmax_scale, int s2_tile, void* workspace_dev,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 KV-cache writer, [P5] section 功能说明与计算公式: for every token i and
+ * head j, with block = slot[i] / block_size and offset = slot[i] % block_size,
+ * copy token i's key row and value row of head j and its key scale (i, j) to
+ * (block, head j, offset) of key_cache_dev, value_cache_dev and
+ * key_scale_cache_dev, in place.  Nothing else is written.
+ *   key_dev     token i, head j, byte d at key_dev[i*key_token_stride + j*k_head_size + d]
+ *               (E4M3 codes; the bytes are copied, never interpreted)
+ *   value_dev   likewise with value_token_stride and v_head_size
+ *   slot_mapping_dev [num_tokens] int32 (slot_bits 32) or int64 (slot_bits 64)
+ *   key_scale_dev    FP32 (i, j) at key_scale_dev[i*key_scale_token_stride + j*key_scale_head_stride]
+ *   layout PA_CACHE_BSND: key_cache  [num_blocks, block_size, num_head, k_head_size],
+ *                         value_cache [num_blocks, block_size, num_head, v_head_size],
+ *                         key_scale_cache [num_blocks, block_size, num_head]
+ *                         (the layouts pa_fp8_decode reads as k_cache / v_cache / k_scale);
+ *          PA_CACHE_BNBD: [num_blocks, num_head, block_size, head_size] and
+ *                         key_scale_cache [num_blocks, num_head, block_size] ([P5]'s
+ *                         [.., 1] shape, same bytes).
+ * Tokens whose slot is < 0 or > num_blocks*block_size - 1 are skipped, as [P5]
+ * prescribes.  Slots must be distinct (repeated slots: one of the tokens wins,
+ * which one is unspecified).  Caller error, not checked: a stride or buffer
+ * that does not cover its rows.  Host checks: every pointer non-NULL
+ * (PA_ERR_NULLPTR); num_tokens >= 1 ([P5] accepts no empty tensor), positive
+ * sizes, slot_bits 32 / 64, a known layout, token strides >= num_head *
+ * head_size, scale strides >= 0 (PA_ERR_INVALID); head sizes and token
+ * strides multiples of 16 bytes, rows and caches 16-byte aligned
+ * (PA_ERR_UNSUPPORTED).  No workspace; asynchronous on `stream`.
+ */
+pa_status_t pa_fp8_scatter_kv_cache(const uint8_t* key_dev, const uint8_t* value_dev, uint8_t* key_cache_dev,
+                                    uint8_t* value_cache_dev, const void* slot_mapping_dev,
+                                    const float* key_scale_dev, float* key_scale_cache_dev, int num_tokens,
+                                    int num_head, int k_head_size, int v_head_size, int num_blocks,
+                                    int block_size, int slot_bits, int layout, int64_t key_token_stride,
+                                    int64_t value_token_stride, int64_t key_scale_token_stride,
+                                    int64_t key_scale_head_stride, void* stream);
 
 /* Message of the last failed call on this host thread ("" if none). */
 const char* pa_fp8_last_error(void);

@@ -74,3 +74,28 @@ def test_workspace_query(lib):
     assert 1 <= s <= 256 and n > 0
     with pytest.raises(binding.PaError):
         binding.workspace_size(2, 1, 8, 3, 128, 128, 6, 256, 1)
+
+
+ALIGNED = ctypes.c_void_p(0x10000)   # 16-byte aligned, never dereferenced
+
+
+def scatter(lib, **over):
+    a = dict(k=ALIGNED, v=ALIGNED, kc=ALIGNED, vc=ALIGNED, slots=ALIGNED, ks=ALIGNED, ksc=ALIGNED,
+             T=4, H=8, dk=128, dv=128, nb=2, bs=16, bits=32, layout=1, kst=1024, vst=1024, kst_s=8, ksh_s=1,
+             stream=None)
+    a.update(over)
+    return lib.pa_fp8_scatter_kv_cache(a["k"], a["v"], a["kc"], a["vc"], a["slots"], a["ks"], a["ksc"], a["T"],
+                                       a["H"], a["dk"], a["dv"], a["nb"], a["bs"], a["bits"], a["layout"],
+                                       a["kst"], a["vst"], a["kst_s"], a["ksh_s"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=None), 1), (dict(slots=None), 1), (dict(ksc=None), 1),
+    (dict(T=0), 2), (dict(H=0), 2), (dict(nb=0), 2), (dict(bs=-1), 2), (dict(bits=16), 2), (dict(layout=2), 2),
+    (dict(kst=512), 2), (dict(vst=1000), 2), (dict(kst_s=-1), 2),
+    (dict(dk=120, kst=960), 3), (dict(kst=1032), 3), (dict(k=ctypes.c_void_p(0x10008)), 3),
+    (dict(bits=64, slots=ctypes.c_void_p(0x10004)), 3),
+])
+def test_scatter_host_validation_codes(lib, over, code):
+    assert scatter(lib, **over) == code
+    assert len(lib.pa_fp8_last_error()) > 0
