@@ -19,7 +19,8 @@ LIB_PATH = os.environ.get("PA_FP8_LIB") or os.path.join(PKG, "libpa_fp8.so")
 PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
 
 EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug",
-           "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode", "pa_fp8_scatter_kv_cache",
+           "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode",
+           "pa_fp8_mla_sparse_decode_kv_split", "pa_fp8_scatter_kv_cache",
            "pa_fp8_last_error", "pa_fp8_version")
 
 PA_CACHE_BSND, PA_CACHE_BNBD = 0, 1
@@ -53,6 +54,8 @@ def lib():
         L.pa_fp8_mla_workspace_size.restype = I
         L.pa_fp8_mla_sparse_decode.argtypes = [P] * 7 + [I] * 7 + [F, I, P, Z, P]
         L.pa_fp8_mla_sparse_decode.restype = I
+        L.pa_fp8_mla_sparse_decode_kv_split.argtypes = [P] * 9 + [I] * 7 + [F, I, P, Z, P]
+        L.pa_fp8_mla_sparse_decode_kv_split.restype = I
         L.pa_fp8_scatter_kv_cache.argtypes = [P] * 7 + [I] * 8 + [ctypes.c_int64] * 4 + [P]
         L.pa_fp8_scatter_kv_cache.restype = I
         L.pa_fp8_last_error.argtypes = []
@@ -179,6 +182,39 @@ def mla_decode(q_nope, q_rope, cache, topk, block_table, kv_act_seqs, softmax_sc
         float(softmax_scale), int(s2_tile), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
+
+
+def mla_decode_kv_split(q_nope, q_rope, kn_quant, kr, kn_scales, topk, block_table, kv_act_seqs, softmax_scale,
+                        s2_tile, s1, out=None, workspace=None, stream=None, block_size=128):
+    """MLA sparse decode over the kv_split cache (kn_quant [rows, 512] uint8,
+    kr [rows, 64] bf16, kn_scales [rows, 4] float32); returns out [B*s1*nq, 512] bf16."""
+    B = int(kv_act_seqs.shape[0])
+    nq = int(q_nope.shape[0]) // (B * s1)
+    K = int(topk.shape[1])
+    _checked_inputs(dict(q_nope=q_nope, q_rope=q_rope, kn_quant=kn_quant, kr=kr, kn_scales=kn_scales, topk=topk,
+                         block_table=block_table, kv_act_seqs=kv_act_seqs, out=out, workspace=workspace))
+    if kn_quant.shape[1] != 512 or kr.shape[1] != 64 or kn_scales.shape[1] != 4:
+        raise ValueError("kv_split planes must be [rows, 512], [rows, 64], [rows, 4]")
+    if out is None:
+        out = torch.empty((B * s1 * nq, 512), dtype=torch.bfloat16, device=q_nope.device)
+    need = mla_workspace_size(B, s1, nq, K, s2_tile)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    _check(lib().pa_fp8_mla_sparse_decode_kv_split(
+        _ptr(q_nope), _ptr(q_rope), _ptr(kn_quant), _ptr(kr), _ptr(kn_scales), _ptr(topk), _ptr(block_table),
+        _ptr(kv_act_seqs), _ptr(out), B, s1, nq, K, block_size, int(block_table.shape[1]),
+        int(kn_quant.shape[0]) // block_size, float(softmax_scale), int(s2_tile), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def mla_decode_kv_split_inputs(inp: dict, out=None, workspace=None, stream=None):
+    """mla_decode_kv_split() on a dict from synth.mla_kv_split(synth.make_mla_inputs(...))."""
+    cfg = inp["cfg"]
+    return mla_decode_kv_split(inp["q_nope"], inp["q_rope"], inp["kn_quant"], inp["kr"], inp["kn_scales"],
+                               inp["topk"], inp["block_table"], inp["kv_act_seqs"], inp["softmax_scale"],
+                               inp.get("s2_tile", cfg.s2_tile), cfg.s1, out=out, workspace=workspace,
+                               stream=stream, block_size=cfg.block_size)
 
 
 def mla_decode_inputs(inp: dict, out=None, workspace=None, stream=None):

@@ -206,6 +206,69 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     return PA_OK;
 }
 
+// MLA sparse decode over three row planes (packed rows: one buffer at offsets
+// 0 / 512 / 640 with stride 672; kv_split: three tensors).
+pa_status_t run_mla(const void* q_nope, const void* q_rope, const uint8_t* nope, const uint8_t* rope,
+                    const uint8_t* scales, int64_t nope_stride, int64_t rope_stride, int64_t scale_stride,
+                    const int32_t* topk_dev, const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
+                    void* out_dev, int B, int s1, int nq, int topk, int block_size, int max_blocks_per_seq,
+                    int num_blocks, float softmax_scale, int s2_tile, void* workspace_dev, size_t workspace_bytes,
+                    void* stream) {
+    if (!q_nope || !q_rope || !topk_dev || !block_table_dev || !kv_act_seqs_dev || !out_dev)
+        return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
+    size_t need = 0;
+    pa_status_t st = pa_fp8_mla_workspace_size(B, s1, nq, topk, s2_tile, &need);
+    if (st != PA_OK) return st;
+    if (block_size != pa::kBlock)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (only 128)", block_size);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID, "max_blocks_per_seq (%d) and num_blocks (%d) must be positive",
+                    max_blocks_per_seq, num_blocks);
+    if ((int64_t)num_blocks * block_size > ((int64_t)1 << 31) - 1)
+        return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size exceeds 2^31 - 1 rows");
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size exceeds 2^30 tokens");
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+        return fail(PA_ERR_INVALID, "softmax_scale must be finite and > 0");
+    auto mis = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; };
+    if (mis(q_nope) || mis(q_rope) || mis(nope) || mis(rope) || mis(scales) || mis(out_dev))
+        return fail(PA_ERR_UNSUPPORTED, "queries, cache planes and output must be 16-byte aligned");
+    if (!workspace_dev || workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace_dev ? workspace_bytes : (size_t)0);
+    pa::MlaParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q_nope = static_cast<const uint16_t*>(q_nope);
+    p.q_rope = static_cast<const uint16_t*>(q_rope);
+    p.nope = nope;
+    p.rope = rope;
+    p.scales = scales;
+    p.nope_stride = nope_stride;
+    p.rope_stride = rope_stride;
+    p.scale_stride = scale_stride;
+    p.topk_idx = topk_dev;
+    p.block_table = block_table_dev;
+    p.seqs = kv_act_seqs_dev;
+    p.out = static_cast<uint16_t*>(out_dev);
+    const size_t rows = (size_t)B * s1 * nq;
+    p.ntiles_max = (topk + s2_tile - 1) / s2_tile;
+    char* base = static_cast<char*>(workspace_dev);
+    p.part_ml = reinterpret_cast<float*>(base);
+    p.part_o = reinterpret_cast<float*>(base + align256(rows * p.ntiles_max * 2 * sizeof(float)));
+    p.B = B;
+    p.s1 = s1;
+    p.nq = nq;
+    p.topk = topk;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.capacity = max_blocks_per_seq * block_size;
+    p.s2_tile = s2_tile;
+    p.softmax_scale = softmax_scale;
+    hipError_t e = pa::launch_mla(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -272,52 +335,26 @@ pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_
                                      float softmax_scale, int s2_tile, void* workspace_dev,
                                      size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
-    if (!q_nope_dev || !q_rope_dev || !cache_dev || !topk_dev || !block_table_dev || !kv_act_seqs_dev ||
-        !out_dev)
-        return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
-    size_t need = 0;
-    pa_status_t st = pa_fp8_mla_workspace_size(B, s1, nq, topk, s2_tile, &need);
-    if (st != PA_OK) return st;
-    if (block_size != pa::kBlock)
-        return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (only 128)", block_size);
-    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
-        return fail(PA_ERR_INVALID, "max_blocks_per_seq (%d) and num_blocks (%d) must be positive",
-                    max_blocks_per_seq, num_blocks);
-    if ((int64_t)num_blocks * block_size > ((int64_t)1 << 31) - 1)
-        return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size exceeds 2^31 - 1 rows");
-    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
-        return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size exceeds 2^30 tokens");
-    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
-        return fail(PA_ERR_INVALID, "softmax_scale must be finite and > 0");
-    if (!workspace_dev || workspace_bytes < need)
-        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                    workspace_dev ? workspace_bytes : (size_t)0);
-    pa::MlaParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.q_nope = static_cast<const uint16_t*>(q_nope_dev);
-    p.q_rope = static_cast<const uint16_t*>(q_rope_dev);
-    p.cache = cache_dev;
-    p.topk_idx = topk_dev;
-    p.block_table = block_table_dev;
-    p.seqs = kv_act_seqs_dev;
-    p.out = static_cast<uint16_t*>(out_dev);
-    const size_t rows = (size_t)B * s1 * nq;
-    p.ntiles_max = (topk + s2_tile - 1) / s2_tile;
-    char* base = static_cast<char*>(workspace_dev);
-    p.part_ml = reinterpret_cast<float*>(base);
-    p.part_o = reinterpret_cast<float*>(base + align256(rows * p.ntiles_max * 2 * sizeof(float)));
-    p.B = B;
-    p.s1 = s1;
-    p.nq = nq;
-    p.topk = topk;
-    p.max_blocks = max_blocks_per_seq;
-    p.num_blocks = num_blocks;
-    p.capacity = max_blocks_per_seq * block_size;
-    p.s2_tile = s2_tile;
-    p.softmax_scale = softmax_scale;
-    hipError_t e = pa::launch_mla(p, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
-    return PA_OK;
+    if (!cache_dev) return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
+    return run_mla(q_nope_dev, q_rope_dev, cache_dev, cache_dev + 512, cache_dev + 640, 672, 672, 672, topk_dev,
+                   block_table_dev, kv_act_seqs_dev, out_dev, B, s1, nq, topk, block_size, max_blocks_per_seq,
+                   num_blocks, softmax_scale, s2_tile, workspace_dev, workspace_bytes, stream);
+}
+
+pa_status_t pa_fp8_mla_sparse_decode_kv_split(const void* q_nope_dev, const void* q_rope_dev,
+                                              const uint8_t* kn_quant_dev, const void* kr_dev,
+                                              const float* kn_scales_dev, const int32_t* topk_dev,
+                                              const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
+                                              void* out_dev, int B, int s1, int nq, int topk, int block_size,
+                                              int max_blocks_per_seq, int num_blocks, float softmax_scale,
+                                              int s2_tile, void* workspace_dev, size_t workspace_bytes,
+                                              void* stream) {
+    g_err[0] = 0;
+    if (!kn_quant_dev || !kr_dev || !kn_scales_dev) return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
+    return run_mla(q_nope_dev, q_rope_dev, kn_quant_dev, static_cast<const uint8_t*>(kr_dev),
+                   reinterpret_cast<const uint8_t*>(kn_scales_dev), 512, 128, 16, topk_dev, block_table_dev,
+                   kv_act_seqs_dev, out_dev, B, s1, nq, topk, block_size, max_blocks_per_seq, num_blocks,
+                   softmax_scale, s2_tile, workspace_dev, workspace_bytes, stream);
 }
 
 pa_status_t pa_fp8_scatter_kv_cache(const uint8_t* key_dev, const uint8_t* value_dev, uint8_t* key_cache_dev,

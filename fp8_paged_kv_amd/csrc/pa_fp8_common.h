@@ -37,7 +37,10 @@ struct DecodeParams {
 struct MlaParams {
     const uint16_t* q_nope;     // [B*s1*nq, 512] bf16
     const uint16_t* q_rope;     // [B*s1*nq, 64] bf16
-    const uint8_t* cache;       // [num_blocks*128, 672] bytes
+    const uint8_t* nope;        // row r: 512 E4M3 codes at nope + r * nope_stride
+    const uint8_t* rope;        // row r: 64 bf16 at rope + r * rope_stride
+    const uint8_t* scales;      // row r: 4 fp32 group scales at scales + r * scale_stride
+    int64_t nope_stride, rope_stride, scale_stride;   // bytes
     const int32_t* topk_idx;    // [B*s1, topk] logical token positions
     const int32_t* block_table; // [B, max_blocks]
     const int32_t* seqs;        // [B]

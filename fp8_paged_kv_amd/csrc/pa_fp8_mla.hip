@@ -21,6 +21,11 @@
 // dequantising V rows on the fly (an 8x8 byte transpose turns row-major codes
 // into MFMA operands).  Each (token, head, tile) leaves an (O, m, l) partial;
 // mla_merge_kernel combines the tiles of each (token, head).
+//
+// The rows are addressed as three planes (nope codes, rope values, group
+// scales), each with its own base and row stride: the packed 672-byte row is
+// the three planes at offsets 0 / 512 / 640 with stride 672, and the page's
+// kv_split sister operator keeps them as three tensors (section 相关算子对比).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,7 +34,7 @@
 
 namespace pa {
 
-constexpr int kMlaNope = 512, kMlaRope = 64, kMlaRow = 672, kMlaHeads = 32;
+constexpr int kMlaNope = 512, kMlaRope = 64, kMlaHeads = 32;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -136,8 +141,10 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
         for (int k = 0; k < 2; ++k) {
             const int li = w * RW + 32 * c + 16 * k + lr;     // this lane's K row (A operand row lr)
             const int row = s_row[li];
-            const uint8_t* rp = a.cache + (int64_t)(row < 0 ? 0 : row) * kMlaRow;
-            const f32x4 gs = *reinterpret_cast<const f32x4*>(rp + 640);
+            const int64_t r = row < 0 ? 0 : row;
+            const uint8_t* rp = a.nope + r * a.nope_stride;
+            const uint8_t* rr = a.rope + r * a.rope_stride;
+            const f32x4 gs = *reinterpret_cast<const f32x4*>(a.scales + r * a.scale_stride);
             f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int pr = 0; pr < 8; ++pr) {
@@ -152,8 +159,8 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
                     acc[hh] = mfma_bf16(k1, qop[hh][2 * pr + 1], acc[hh]);
                 }
             }
-            const i32x4 r0 = *reinterpret_cast<const i32x4*>(rp + kMlaNope + 32 * lg);
-            const i32x4 r1 = *reinterpret_cast<const i32x4*>(rp + kMlaNope + 32 * lg + 16);
+            const i32x4 r0 = *reinterpret_cast<const i32x4*>(rr + 32 * lg);
+            const i32x4 r1 = *reinterpret_cast<const i32x4*>(rr + 32 * lg + 16);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 acc[hh] = mfma_bf16(__builtin_bit_cast(bf16x8, r0), qop[hh][16], acc[hh]);
@@ -216,9 +223,9 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int row = s_row[32 * bi + chunk_token(lg, j)];
-            const uint8_t* rp = a.cache + (int64_t)(row < 0 ? 0 : row) * kMlaRow;
-            const uint2 x = *reinterpret_cast<const uint2*>(rp + 128 * w + 8 * lr);
-            const float g = *reinterpret_cast<const float*>(rp + 640 + 4 * w);
+            const int64_t r = row < 0 ? 0 : row;
+            const uint2 x = *reinterpret_cast<const uint2*>(a.nope + r * a.nope_stride + 128 * w + 8 * lr);
+            const float g = *reinterpret_cast<const float*>(a.scales + r * a.scale_stride + 4 * w);
             xl[j] = row < 0 ? 0u : x.x;            // positions past n: zero codes (P is 0 there)
             xh[j] = row < 0 ? 0u : x.y;
             scj[j] = g;

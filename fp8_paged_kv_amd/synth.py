@@ -326,6 +326,19 @@ def make_mla_inputs(cfg: MlaConfig, device="cpu", seed: Optional[int] = None,
     )
 
 
+def mla_kv_split(inp: dict) -> dict:
+    """The same cache as [P2]'s kv_split sister operator holds it: three tensors
+    (section 相关算子对比) -- kn_quant [rows, 512] e4m3 codes, kr [rows, 64] bf16,
+    kn_scales [rows, 4] fp32 -- cut from the packed 672-byte rows (bytes
+    0..511, 512..639 and 640..655)."""
+    cache = inp["cache"]
+    rows = cache.shape[0]
+    return dict(inp,
+                kn_quant=cache[:, :MLA_NOPE].contiguous(),
+                kr=cache[:, MLA_NOPE:MLA_NOPE + 2 * MLA_ROPE].contiguous().view(torch.bfloat16).view(rows, MLA_ROPE),
+                kn_scales=cache[:, 640:656].contiguous().view(torch.float32).view(rows, MLA_GROUPS))
+
+
 def gqa_algorithmic_bytes(cfg: GqaConfig, seqs: Sequence[int]) -> int:
     """Bytes the decode must move at least once: for every valid (token, kv
     head) its K row, V row and k_scale; v_scale per (batch, kv head); Q

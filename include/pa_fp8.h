@@ -175,6 +175,25 @@ pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * pa_fp8_mla_sparse_decode with the cache as the three tensors of [P2]'s
+ * kv_split sister operator (section 相关算子对比) instead of packed rows:
+ *   kn_quant_dev  [num_blocks*128, 512] E4M3 codes (row stride 512 bytes)
+ *   kr_dev        [num_blocks*128, 64]  bf16        (row stride 128 bytes)
+ *   kn_scales_dev [num_blocks*128, 4]   fp32 group scales (row stride 16 bytes)
+ * Same computation, same results bit for bit as the packed layout holding the
+ * same values; same arguments, checks and workspace otherwise.  All three
+ * planes (and q, out) must be 16-byte aligned (PA_ERR_UNSUPPORTED).
+ */
+pa_status_t pa_fp8_mla_sparse_decode_kv_split(const void* q_nope_dev, const void* q_rope_dev,
+                                              const uint8_t* kn_quant_dev, const void* kr_dev,
+                                              const float* kn_scales_dev, const int32_t* topk_dev,
+                                              const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
+                                              void* out_dev, int B, int s1, int nq, int topk, int block_size,
+                                              int max_blocks_per_seq, int num_blocks, float softmax_scale,
+                                              int s2_tile, void* workspace_dev, size_t workspace_bytes,
+                                              void* stream);
+
+/*
  * FP8 KV-cache writer, [P5] section 功能说明与计算公式: for every token i and
  * head j, with block = slot[i] / block_size and offset = slot[i] % block_size,
  * copy token i's key row and value row of head j and its key scale (i, j) to

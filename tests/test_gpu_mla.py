@@ -88,3 +88,30 @@ def test_mla_full_size_sampled_batches(B, oracle_mod):
     got = gpu_out_float(_run(B, inp, "config4")).reshape(cfg.B * cfg.s1, cfg.nq, 512)
     ref = oracle_mod.mla_decode(inp, b_range=(0, 2))["out_bf16"].reshape(cfg.B * cfg.s1, cfg.nq, 512)
     compare(got[:2 * cfg.s1], ref[:2 * cfg.s1], "mla config4 batches 0-1")
+
+
+def _run_split(B, inp_h, tag):
+    print(f"[gpu] mla kv_split {tag} seqs={inp_h['kv_act_seqs'].tolist()[:8]}", flush=True)
+    out = B.mla_decode_kv_split_inputs(to_device(synth.mla_kv_split(inp_h)))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("s2_tile", [128, 512])
+def test_mla_kv_split_matches_packed_and_oracle(B, oracle_mod, s2_tile):
+    """The kv_split layout (three tensors) gives the packed layout's output bit for
+    bit on the same values, and matches the oracle."""
+    inp = synth.make_mla_inputs(_cfg(f"mla-split-t{s2_tile}", s2_tile=s2_tile, seq_lens=(100, 700, 1500), B=3,
+                                     num_blocks=40, seed=13))
+    packed = _run(B, inp, f"packed tile{s2_tile}")
+    split = _run_split(B, inp, f"tile{s2_tile}")
+    assert torch.equal(packed, split)
+    compare(gpu_out_float(split), oracle_mod.mla_decode(inp)["out_bf16"], f"mla kv_split s2_tile={s2_tile}")
+
+
+def test_mla_kv_split_full_size(B, oracle_mod):
+    cfg = synth.CONFIGS[4]
+    inp = synth.make_mla_inputs(cfg)
+    got = gpu_out_float(_run_split(B, inp, "config4")).reshape(cfg.B * cfg.s1, cfg.nq, 512)
+    ref = oracle_mod.mla_decode(inp, b_range=(2, 4))["out_bf16"].reshape(cfg.B * cfg.s1, cfg.nq, 512)
+    compare(got[2 * cfg.s1:4 * cfg.s1], ref[2 * cfg.s1:4 * cfg.s1], "mla kv_split config4 batches 2-3")

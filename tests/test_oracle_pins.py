@@ -424,3 +424,21 @@ def test_mla_valid_count_formula(oracle_mod):
                 got = res["out"][(b * 2 + s) * cfg.nq + hq]
                 np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
     assert np.all(res["out"][(1 * 2 + 0) * cfg.nq:(1 * 2 + 1) * cfg.nq] == 0)   # seq 1, s 0 -> n = 0
+
+
+def test_mla_kv_split_planes_follow_the_row_layout():
+    """synth.mla_kv_split cuts the three kv_split tensors at the byte ranges the
+    page's 672-byte row layout names (nope, rope, scales)."""
+    lay = GOLDEN["mla_row_layout"]
+    cfg = synth.MlaConfig("split-pin", B=1, s1=1, nq=32, topk=64, seq_range=None, num_blocks=2,
+                          max_blocks_per_seq=2, seq_lens=(100,), seed=2)
+    inp = synth.make_mla_inputs(cfg)
+    sp = synth.mla_kv_split(inp)
+    cache = inp["cache"].numpy()
+    lo, hi = lay["nope"]
+    assert np.array_equal(sp["kn_quant"].numpy(), cache[:, lo:hi])
+    lo, hi = lay["rope_bf16"]
+    assert np.array_equal(sp["kr"].view(torch.int16).numpy().view(np.uint8).reshape(cache.shape[0], -1),
+                          cache[:, lo:hi])
+    lo, hi = lay["scales_fp32"]
+    assert np.array_equal(sp["kn_scales"].numpy().view(np.uint8).reshape(cache.shape[0], -1), cache[:, lo:hi])
