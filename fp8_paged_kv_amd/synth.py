@@ -22,6 +22,10 @@ Sources for the layouts and scale rules used to *prepare* inputs:
      反量化算子" (www.mhpn.cn/news/2272720), section "核心参数与 KV Cache 布局":
      the 672-byte cache row [0:512) e4m3 nope, [512:640) 64 bf16 rope,
      [640:656) four fp32 group scales, 16 bytes of padding.
+[P3] the web page "CANN ops-transformer aclnnKvCompressEpilog 算子详解"
+     (www.lmnt.cn/news/267091), section 参数说明: x [tokens, d] bf16 with
+     d % 64 == 0, slotMapping [tokens] int32 / int64 (-1 = skip), cache
+     [blockNum, blockSize, 1, headDim] uint8.
 [P5] the web page on ops-transformer's scatter_pa_kv_cache_with_k_scale
      (www.lmnt.cn/news/278797), section 函数原型: key / value
      [num_tokens, num_head, head_size] FP8, key_scale [num_tokens, num_head]
@@ -444,3 +448,51 @@ def prefill_slots(cfg: GqaConfig, device="cpu", seed: Optional[int] = None) -> d
         parts.append(table[b, p // bs].to(torch.int64) * bs + p % bs)
     slots = torch.cat(parts) if parts else torch.zeros(0, dtype=torch.int64)
     return dict(slots=slots.to(torch.int32).to(device), seqs=seqs, block_table=table)
+
+
+# ------------------------------------------------------- KvCompressEpilog
+
+@dataclass(frozen=True)
+class EpilogConfig:
+    """Shape recipe of one KvCompressEpilog call ([P3])."""
+    name: str
+    num_tokens: int
+    d: int
+    block_num: int
+    block_size: int
+    head_dim: int
+    quant_mode: int = 1
+    round_scale: bool = True
+    slot_bits: int = 32
+    skip: int = 0                 # tokens given slot -1
+    block_pad: int = 0            # extra bytes between blocks (a cache viewed inside a larger buffer)
+    seed: int = 0
+
+
+def make_epilog_inputs(cfg: EpilogConfig, device="cpu", seed: Optional[int] = None) -> dict:
+    """Draw one seeded KvCompressEpilog call.
+
+    x ~ N(0,1) in fp32 rounded to bf16, with per-(token, 64-column group) gains
+    drawn log-uniformly over 2^-20 .. 2^20 (so the scales span many binades)
+    and one group in 16 set to zero; slots are distinct (first tokens of a
+    random permutation of the pool), ``skip`` of them -1; the cache starts as
+    random bytes.  The cache is a flat byte buffer of block_num blocks of
+    block_size * head_dim + block_pad bytes."""
+    seed = cfg.seed if seed is None else seed
+    g = _gen(device, seed)
+    T, d = cfg.num_tokens, cfg.d
+    nslots = cfg.block_num * cfg.block_size
+    assert T <= nslots
+    x = torch.randn((T, d // 64, 64), generator=g, device=device)
+    gain = torch.exp2(torch.rand((T, d // 64, 1), generator=g, device=device) * 40 - 20)
+    zero = torch.rand((T, d // 64, 1), generator=g, device=device) < 1 / 16
+    x = torch.where(zero, torch.zeros_like(x), x * gain).reshape(T, d).to(torch.bfloat16)
+    slots = torch.randperm(nslots, generator=g, device=device)[:T].to(torch.int64)
+    if cfg.skip:
+        which = torch.randperm(T, generator=g, device=device)[: cfg.skip]
+        slots[which] = -1
+    slots = slots.to(torch.int32 if cfg.slot_bits == 32 else torch.int64)
+    block_stride = cfg.block_size * cfg.head_dim + cfg.block_pad
+    cache = torch.randint(0, 256, (cfg.block_num * block_stride,), generator=g, device=device,
+                          dtype=torch.int32).to(torch.uint8)
+    return dict(cfg=cfg, x=x, slot_mapping=slots, cache=cache, block_stride=block_stride)

@@ -55,6 +55,12 @@ def lib():
         L.oracle_pa_fp8_decode_rows.restype = I
         L.oracle_mla_sparse_decode.argtypes = [P] * 6 + [I] * 7 + [ctypes.c_double] + [I] * 3 + [P] * 2
         L.oracle_mla_sparse_decode.restype = I
+        L.oracle_kv_compress_row_bytes.argtypes = [I, I]
+        L.oracle_kv_compress_row_bytes.restype = I
+        L.oracle_kv_compress_cache_col.argtypes = [I, I]
+        L.oracle_kv_compress_cache_col.restype = I
+        L.oracle_kv_compress_epilog.argtypes = [P, P, P] + [I] * 5 + [ctypes.c_int64, I, I]
+        L.oracle_kv_compress_epilog.restype = I
         L.oracle_scatter_kv_cache.argtypes = [P] * 7 + [I] * 7 + [ctypes.c_int64] * 4
         L.oracle_scatter_kv_cache.restype = I
         _lib = L
@@ -252,3 +258,34 @@ def _slots64(slot_mapping) -> np.ndarray:
     except ImportError:
         pass
     return np.asarray(slot_mapping).astype(np.int64)
+
+
+def kv_compress_row_bytes(d: int, mode: int) -> int:
+    return lib().oracle_kv_compress_row_bytes(int(d), int(mode))
+
+
+def kv_compress_cache_col(d: int, mode: int) -> int:
+    return lib().oracle_kv_compress_cache_col(int(d), int(mode))
+
+
+def kv_compress_epilog(cache, x, slot_mapping, mode: int, round_scale: bool = True, block_stride=None) -> dict:
+    """[P3] KvCompressEpilog modes 0/1 on a copy of ``cache``.
+
+    cache: [block_num, block_size, 1, head_dim] uint8 (a block stride in bytes
+    may be given for a cache viewed inside a larger buffer: then ``cache`` is
+    the flat buffer); x: [tokens, d] bf16 (or its int16 bits); slot_mapping
+    [tokens] int32 / int64.  Returns the updated copy and the written count."""
+    c = _np(cache, np.uint8).copy()
+    xs = _np(x, np.uint16)
+    slots = np.ascontiguousarray(_slots64(slot_mapping))
+    T, d = xs.shape
+    if block_stride is None:
+        nb, bs, _, hd = c.shape
+        stride = bs * hd
+    else:
+        nb, bs, hd, stride = block_stride
+    n = lib().oracle_kv_compress_epilog(_ptr(c), _ptr(xs), _ptr(slots), T, d, nb, bs, hd, stride, int(mode),
+                                        1 if round_scale else 0)
+    if n < 0:
+        raise ValueError("oracle_kv_compress_epilog rejected its arguments")
+    return dict(cache=c, written=n)

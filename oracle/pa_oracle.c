@@ -28,6 +28,19 @@
  *      - section 约束说明 and the SIMT kernel paragraph: slots below 0 or above
  *        num_blocks * block_size - 1 are skipped; repeated slots are the
  *        caller's error (no result is promised).
+ * [P3] web page "CANN ops-transformer aclnnKvCompressEpilog 算子详解"
+ *      (www.lmnt.cn/news/267091).
+ *      - section 功能说明 (semantics): bf16 rows x [tokens, d] are quantised and
+ *        written in place to the cache row of their slot; slot -1 skips the
+ *        token; the last 64 columns are the rope part, the first d - 64 the
+ *        nope part; quant modes 0 (FP8 groups, bf16 scale) and 1 (FP8 groups,
+ *        e8m0 power-of-two scale, roundScale rounds the scale up to a power
+ *        of two);
+ *      - section 计算公式: scale_g = max|x_g| / 448, q = round(x / scale_g);
+ *      - section 约束说明 and the kvCacheCol walkthrough: row layout
+ *        [rope bf16, 128 B][nope e4m3, d - 64 B][one scale per 64 columns,
+ *        2 B (mode 0) or 1 B (mode 1)]; the cache row must hold kvCacheCol
+ *        bytes (mode 1: the written bytes; mode 0: rounded up to 32).
  * [P2] web page "PyPTO-Gym 算子实战DeepSeek V32 MLA 的 Sparse Attention FP8 反量化
  *      算子" (www.mhpn.cn/news/2272720).
  *      - section 核心参数与 KV Cache 布局: 672-byte row = 512 e4m3 nope,
@@ -66,6 +79,18 @@
  *        decode reads -- and BNBD [block, head, offset, d] with scales
  *        [block, head, offset] -- [P5]'s documented layout.
  *  R-dup with a repeated slot the later token wins here (tests never repeat).
+ *  R-ep-grp  in modes 0 / 1 a group is 64 nope columns whatever quantGroupSize
+ *        says ([P3]'s row-size formula counts ceil((d - 64) / 64) scales;
+ *        quantGroupSize governs mode 2).
+ *  R-ep-scale scale = fp32(amax / 448).  Mode 0 stores bf16(scale) (RNE) and
+ *        divides by the stored bf16 value; mode 1 stores 2^k as e8m0 (code
+ *        k + 127, k clamped to [-127, 127]) with k = ceil(log2 scale) when
+ *        roundScale, else floor(log2 scale), and divides by 2^k.  The
+ *        quotient is an fp32 division; codes are E4M3 RNE saturating at 448.
+ *  R-ep-zero an all-zero group (or a stored mode-0 scale of 0) gives zero
+ *        codes; its stored scale is bf16 0 (mode 0) or e8m0 code 0 (mode 1).
+ *  R-ep-pad  bytes of a cache row past the written ones are left untouched.
+ *  R-ep-slot slots < 0 or >= blockNum * blockSize are skipped.
  */
 #include <math.h>
 #include <stdint.h>
@@ -560,6 +585,92 @@ int oracle_scatter_kv_cache(const uint8_t* key, const uint8_t* value,
             for (int d = 0; d < v_head_size; ++d)
                 value_cache[vpos + d] = value[(int64_t)i * value_token_stride + (int64_t)j * v_head_size + d];
             key_scale_cache[spos] = key_scale[(int64_t)i * ks_token_stride + (int64_t)j * ks_head_stride];
+        }
+        ++written;
+    }
+    return written;
+}
+
+/* --------------------------------------------- [P3] KvCompressEpilog modes 0/1 */
+
+/* Bytes written per token (the page's concatCol): rope 128 B, d - 64 FP8
+ * codes, one scale per 64 nope columns (2 B in mode 0, 1 B in mode 1). */
+int oracle_kv_compress_row_bytes(int d, int mode)
+{
+    if (d <= 64 || (mode != 0 && mode != 1))
+        return -1;
+    const int groups = (d - 64 + 63) / 64;
+    return (d - 64) + 128 + groups * (mode == 0 ? 2 : 1);
+}
+
+/* Minimum cache row (kvCacheCol): mode 1 as written, mode 0 rounded up to 32. */
+int oracle_kv_compress_cache_col(int d, int mode)
+{
+    int c = oracle_kv_compress_row_bytes(d, mode);
+    if (c < 0)
+        return -1;
+    return mode == 1 ? c : (c + 31) / 32 * 32;
+}
+
+/*
+ * In-place quantising scatter of bf16 rows x [num_tokens, d] (R-ep-*):
+ * token t with slot s in [0, block_num * block_size) writes row
+ * cache + (s / block_size) * block_stride + (s % block_size) * head_dim.
+ * Returns the number of tokens written, or -1 on a bad argument.
+ */
+int oracle_kv_compress_epilog(uint8_t* cache, const uint16_t* x, const int64_t* slots, int num_tokens, int d,
+                              int block_num, int block_size, int head_dim, int64_t block_stride, int mode,
+                              int round_scale)
+{
+    const int row_bytes = oracle_kv_compress_row_bytes(d, mode);
+    if (row_bytes < 0 || d % 64 != 0 || d > 8192 || num_tokens < 0 || block_num <= 0 || block_size <= 0 ||
+        head_dim < oracle_kv_compress_cache_col(d, mode) || block_stride < (int64_t)block_size * head_dim)
+        return -1;
+    const int64_t num_slots = (int64_t)block_num * block_size;
+    const int nope = d - 64, groups = nope / 64;
+    int written = 0;
+    for (int t = 0; t < num_tokens; ++t) {
+        const int64_t slot = slots[t];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        uint8_t* row = cache + (slot / block_size) * block_stride + (slot % block_size) * head_dim;
+        const uint16_t* xr = x + (int64_t)t * d;
+        for (int c = 0; c < 64; ++c) {                 /* rope: the last 64 columns, bf16 bytes */
+            row[2 * c] = (uint8_t)(xr[nope + c] & 0xFF);
+            row[2 * c + 1] = (uint8_t)(xr[nope + c] >> 8);
+        }
+        for (int g = 0; g < groups; ++g) {
+            double amax = 0.0;
+            for (int c = 0; c < 64; ++c) {
+                double v = fabs(oracle_bf16_decode(xr[64 * g + c]));
+                if (v > amax) amax = v;
+            }
+            const double scale = round_to_fp32(amax / OR_E4M3_MAX);
+            double used;
+            uint8_t* sp = row + 128 + nope;
+            if (mode == 0) {
+                uint16_t sb = oracle_bf16_encode(scale);
+                sp[2 * g] = (uint8_t)(sb & 0xFF);
+                sp[2 * g + 1] = (uint8_t)(sb >> 8);
+                used = oracle_bf16_decode(sb);
+            } else {
+                int k = -127;
+                if (scale > 0.0) {
+                    int e2;
+                    double f = frexp(scale, &e2);      /* scale = f * 2^e2, f in [0.5, 1) */
+                    k = (round_scale && f != 0.5) ? e2 : e2 - 1;
+                    if (k < -127) k = -127;
+                    if (k > 127) k = 127;
+                }
+                sp[g] = (uint8_t)(k + 127);
+                used = (scale > 0.0) ? ldexp(1.0, k) : 0.0;
+            }
+            for (int c = 0; c < 64; ++c) {
+                double q = 0.0;
+                if (used > 0.0)
+                    q = round_to_fp32(oracle_bf16_decode(xr[64 * g + c]) / used);
+                row[128 + 64 * g + c] = oracle_e4m3_encode(q);
+            }
         }
         ++written;
     }
