@@ -41,8 +41,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
-    ap.add_argument("--op", choices=["decode", "scatter"], default="decode",
-                    help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write)")
+    ap.add_argument("--op", choices=["decode", "scatter", "epilog"], default="decode",
+                    help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
+                         "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows")
     ap.add_argument("--splits", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled by the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,6 +147,8 @@ def main():
     binding.lib()
     if args.op == "scatter":
         return run_scatter(args)
+    if args.op == "epilog":
+        return run_epilog(args)
     if args.config == 4:
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
@@ -347,6 +350,41 @@ def run_scatter(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "pa::scatter_kv_kernel<int, 0>"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_epilog(args):
+    """KvCompressEpilog, quant mode 1 (e8m0 scales, roundScale): 131072 bf16 rows
+    of the MLA latent width d = 576 (512 nope + 64 rope) written into a
+    1024 x 128-row cache of 649-byte rows (the 648 bytes a row needs, one spare)."""
+    import torch
+    from fp8_paged_kv_amd import binding, synth
+    cfg = synth.EpilogConfig("epilog-bench", num_tokens=131072, d=576, block_num=1024, block_size=128,
+                             head_dim=649, quant_mode=1, round_scale=True, seed=9)
+    inp = synth.make_epilog_inputs(cfg, device="cuda")
+
+    def call(stream):
+        binding.epilog_inputs(inp, stream=stream)
+
+    wall, ev = _time(call, args.steps, args.warmup)
+    row_bytes = (cfg.d - 64) + 128 + (cfg.d - 64) // 64
+    nbytes = cfg.num_tokens * (2 * cfg.d + row_bytes + 4)          # read x and the slot, write the row
+    ms = wall / args.steps * 1e3
+    mean = sum(ev) / len(ev)
+    achieved = nbytes / (mean * 1e-3) / 1e9
+    line = {
+        "metric": "KvCompressEpilog mode 1, algorithmic GB/s", "value": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 -> fp8 e4m3 codes, fp32 scale arithmetic", "data": "synthetic",
+        "config": {"workload": "kv-compress-epilog-mode1-d576-tokens131072", "num_tokens": cfg.num_tokens,
+                   "d": cfg.d, "block_num": cfg.block_num, "block_size": cfg.block_size, "head_dim": cfg.head_dim,
+                   "quant_mode": 1, "round_scale": True, "algorithmic_bytes_per_call": nbytes},
+        "event_us_per_call": {"mean": round(mean * 1e3, 2), "median": round(ev[len(ev) // 2] * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa::kv_compress_epilog_kernel<int, 1>"},
     }
     print(json.dumps(line), flush=True)
 

@@ -21,6 +21,7 @@ PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_
 EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug",
            "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode",
            "pa_fp8_mla_sparse_decode_kv_split", "pa_fp8_scatter_kv_cache",
+           "pa_fp8_kv_compress_epilog_workspace_size", "pa_fp8_kv_compress_epilog",
            "pa_fp8_last_error", "pa_fp8_version")
 
 PA_CACHE_BSND, PA_CACHE_BNBD = 0, 1
@@ -58,6 +59,10 @@ def lib():
         L.pa_fp8_mla_sparse_decode_kv_split.restype = I
         L.pa_fp8_scatter_kv_cache.argtypes = [P] * 7 + [I] * 8 + [ctypes.c_int64] * 4 + [P]
         L.pa_fp8_scatter_kv_cache.restype = I
+        L.pa_fp8_kv_compress_epilog_workspace_size.argtypes = [I] * 5 + [ctypes.c_int64, I, I, P]
+        L.pa_fp8_kv_compress_epilog_workspace_size.restype = I
+        L.pa_fp8_kv_compress_epilog.argtypes = [P] * 3 + [I] * 5 + [ctypes.c_int64] + [I] * 4 + [F, P, Z, P]
+        L.pa_fp8_kv_compress_epilog.restype = I
         L.pa_fp8_last_error.argtypes = []
         L.pa_fp8_last_error.restype = ctypes.c_char_p
         L.pa_fp8_version.argtypes = []
@@ -265,3 +270,37 @@ def scatter_inputs(inp: dict, stream=None):
     (updates the dict's caches in place)."""
     scatter_kv_cache(inp["key"], inp["value"], inp["key_cache"], inp["value_cache"], inp["slot_mapping"],
                      inp["key_scale"], inp["key_scale_cache"], inp["cfg"].layout, stream=stream)
+
+
+def kv_compress_epilog(cache, x, slot_mapping, block_num, block_size, head_dim, block_stride=None, quant_mode=1,
+                       round_scale=True, quant_group_size=64, x_scale=1.0, stream=None):
+    """KvCompressEpilog modes 0/1 (pa_fp8_kv_compress_epilog), in place.
+
+    cache: a uint8 tensor holding block_num blocks (block_stride bytes apart,
+    default block_size * head_dim) of block_size rows of head_dim bytes --
+    e.g. [block_num, block_size, 1, head_dim]; x [tokens, d] bf16;
+    slot_mapping [tokens] int32 / int64."""
+    T, d = (int(v) for v in x.shape)
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 tensor")
+    if cache.dtype != torch.uint8 or slot_mapping.dtype not in (torch.int32, torch.int64):
+        raise ValueError("cache must be uint8, slot_mapping int32 or int64")
+    stride = block_size * head_dim if block_stride is None else int(block_stride)
+    if cache.numel() < (block_num - 1) * stride + block_size * head_dim:
+        raise ValueError("cache smaller than its blocks")
+    _checked_inputs(dict(cache=cache, x=x, slot_mapping=slot_mapping))
+    n = ctypes.c_size_t(0)
+    _check(lib().pa_fp8_kv_compress_epilog_workspace_size(T, d, block_num, block_size, head_dim, stride,
+                                                          quant_group_size, quant_mode, ctypes.byref(n)))
+    _check(lib().pa_fp8_kv_compress_epilog(
+        _ptr(cache), _ptr(x), _ptr(slot_mapping), T, d, block_num, block_size, head_dim, stride,
+        32 if slot_mapping.dtype == torch.int32 else 64, quant_group_size, quant_mode, 1 if round_scale else 0,
+        float(x_scale), None, 0, _stream(stream)))
+
+
+def epilog_inputs(inp: dict, stream=None):
+    """kv_compress_epilog() on a dict from synth.make_epilog_inputs (updates inp["cache"] in place)."""
+    c = inp["cfg"]
+    kv_compress_epilog(inp["cache"], inp["x"], inp["slot_mapping"], c.block_num, c.block_size, c.head_dim,
+                       block_stride=inp["block_stride"], quant_mode=c.quant_mode, round_scale=c.round_scale,
+                       stream=stream)

@@ -411,6 +411,68 @@ pa_status_t pa_fp8_scatter_kv_cache(const uint8_t* key_dev, const uint8_t* value
     return PA_OK;
 }
 
+pa_status_t pa_fp8_kv_compress_epilog_workspace_size(int num_tokens, int d, int block_num, int block_size,
+                                                     int head_dim, int64_t block_stride, int quant_group_size,
+                                                     int quant_mode, size_t* bytes_host) {
+    g_err[0] = 0;
+    if (!bytes_host) return fail(PA_ERR_NULLPTR, "bytes_host is NULL");
+    if (num_tokens <= 0 || block_num <= 0 || block_size <= 0 || head_dim <= 0)
+        return fail(PA_ERR_INVALID, "sizes must be positive (num_tokens=%d block_num=%d block_size=%d head_dim=%d)",
+                    num_tokens, block_num, block_size, head_dim);
+    if (d % 64 != 0 || d <= 64 || d > 8192)
+        return fail(PA_ERR_INVALID, "d must be a multiple of 64 in (64, 8192] (got %d)", d);
+    if (quant_mode < 0 || quant_mode > 2) return fail(PA_ERR_INVALID, "quant_mode must be 0, 1 or 2 (got %d)", quant_mode);
+    if (quant_mode == 2) {
+        if (quant_group_size != 16 && quant_group_size != 32 && quant_group_size != 64)
+            return fail(PA_ERR_INVALID, "mode 2 takes quant_group_size 16, 32 or 64 (got %d)", quant_group_size);
+        return fail(PA_ERR_UNSUPPORTED, "quant_mode 2 (hifloat8 rope, FP4 nope) is not built");
+    }
+    const int groups = (d - 64 + 63) / 64;
+    const int written = (d - 64) + 128 + groups * (quant_mode == 0 ? 2 : 1);
+    const int col = quant_mode == 1 ? written : (written + 31) / 32 * 32;
+    if (head_dim < col)
+        return fail(PA_ERR_INVALID, "head_dim %d below the %d bytes a row of mode %d needs", head_dim, col, quant_mode);
+    if (block_stride < (int64_t)block_size * head_dim)
+        return fail(PA_ERR_INVALID, "block_stride must be >= block_size * head_dim");
+    *bytes_host = 0;
+    return PA_OK;
+}
+
+pa_status_t pa_fp8_kv_compress_epilog(uint8_t* cache_dev, const void* x_dev, const void* slot_mapping_dev,
+                                      int num_tokens, int d, int block_num, int block_size, int head_dim,
+                                      int64_t block_stride, int slot_bits, int quant_group_size, int quant_mode,
+                                      int round_scale, float x_scale, void* workspace_dev, size_t workspace_bytes,
+                                      void* stream) {
+    (void)x_scale;                     // used by mode 2 only
+    (void)workspace_dev;
+    (void)workspace_bytes;
+    g_err[0] = 0;
+    if (!cache_dev || !x_dev || !slot_mapping_dev) return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
+    size_t need = 0;
+    pa_status_t st = pa_fp8_kv_compress_epilog_workspace_size(num_tokens, d, block_num, block_size, head_dim,
+                                                              block_stride, quant_group_size, quant_mode, &need);
+    if (st != PA_OK) return st;
+    if (slot_bits != 32 && slot_bits != 64) return fail(PA_ERR_INVALID, "slot_bits must be 32 or 64 (got %d)", slot_bits);
+    if ((reinterpret_cast<uintptr_t>(x_dev) & 15) || (reinterpret_cast<uintptr_t>(slot_mapping_dev) & (slot_bits / 8 - 1)))
+        return fail(PA_ERR_UNSUPPORTED, "x must be 16-byte aligned and slots aligned to their width");
+    pa::EpilogParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.cache = cache_dev;
+    p.x = static_cast<const uint16_t*>(x_dev);
+    p.slots = slot_mapping_dev;
+    p.num_tokens = num_tokens;
+    p.num_slots = (int64_t)block_num * block_size;
+    p.block_stride = block_stride;
+    p.d = d;
+    p.block_size = block_size;
+    p.head_dim = head_dim;
+    p.mode = quant_mode;
+    p.round_scale = round_scale ? 1 : 0;
+    hipError_t e = pa::launch_kv_compress_epilog(p, slot_bits, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 const char* pa_fp8_last_error(void) { return g_err; }
 
 const char* pa_fp8_version(void) { return "pa_fp8 0.1 gfx950"; }

@@ -65,7 +65,17 @@ struct ScatterParams {
     int64_t k_stride, v_stride, ks_token_stride, ks_head_stride;
 };
 
+// KvCompressEpilog modes 0 / 1 (quantising slot scatter of bf16 rows).
+struct EpilogParams {
+    uint8_t* cache;             // row of slot s: cache + (s / block_size) * block_stride + (s % block_size) * head_dim
+    const uint16_t* x;          // [num_tokens, d] bf16
+    const void* slots;          // [num_tokens] int32 or int64
+    int64_t num_tokens, num_slots, block_stride;
+    int d, block_size, head_dim, mode, round_scale;
+};
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, bool debug);
+hipError_t launch_kv_compress_epilog(const EpilogParams& p, int slot_bits, hipStream_t stream);
 hipError_t launch_scatter_kv(const ScatterParams& p, int slot_bits, int layout, hipStream_t stream);
 bool mla_supported(int nq, int s2_tile);
 hipError_t launch_mla(const MlaParams& p, hipStream_t stream);

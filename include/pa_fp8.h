@@ -15,6 +15,7 @@
  *      — the two-phase convention (query the workspace size, then run with
  *      a caller-owned workspace) and distinct null-pointer / invalid-argument
  *      status codes.
+ *      Also the KvCompressEpilog operator itself (quant modes 0 and 1).
  * [P5] the ops-transformer scatter_pa_kv_cache_with_k_scale page
  *      (www.lmnt.cn/news/278797) — the FP8 KV-cache writer: section
  *      功能说明与计算公式 (slot -> block, offset), section 函数原型 and 约束说明
@@ -228,6 +229,48 @@ pa_status_t pa_fp8_scatter_kv_cache(const uint8_t* key_dev, const uint8_t* value
                                     int block_size, int slot_bits, int layout, int64_t key_token_stride,
                                     int64_t value_token_stride, int64_t key_scale_token_stride,
                                     int64_t key_scale_head_stride, void* stream);
+
+/*
+ * KvCompressEpilog, quant modes 0 and 1 ([P3] sections 功能说明, 计算公式,
+ * 约束说明).  Two-phase like [P3]: the size query validates the shape and
+ * reports the workspace (always 0 bytes here); workspace arguments of the run
+ * call are ignored.
+ *
+ * For every token t whose slot s = slot_mapping[t] lies in
+ * [0, block_num * block_size) (others, [P3]'s -1 included, are skipped), the
+ * bf16 row x[t, 0:d] is written at
+ *     row = cache_dev + (s / block_size) * block_stride + (s % block_size) * head_dim
+ * as [rope: the last 64 values, bf16, 128 B][nope codes, d - 64 B][scales]:
+ *   per group g of 64 nope columns, scale = fp32(max|x_g| / 448);
+ *   mode 0: stored bf16(scale) (RNE, 2 B), code = E4M3(fp32(x / stored));
+ *   mode 1: stored e8m0 2^k (1 B, code k + 127, k in [-127, 127]),
+ *           k = ceil(log2 scale) when round_scale, else floor(log2 scale),
+ *           code = E4M3(fp32(x / 2^k));
+ *   codes round to nearest even and saturate at +-448; an all-zero group
+ *   gives zero codes (stored scale 0 / e8m0 code 0).  Bytes of the row past
+ *   the written ones are not touched; nothing outside the rows of valid
+ *   slots is touched.
+ *   cache_dev  [block_num] blocks of block_size rows of head_dim bytes, block
+ *              starts block_stride bytes apart (>= block_size * head_dim)
+ *   x_dev      [num_tokens, d] bf16, 16-byte aligned
+ *   slot_mapping_dev [num_tokens] int32 (slot_bits 32) or int64 (64); slots
+ *              must be distinct (repeats: unspecified).
+ * Host checks: NULL pointers (PA_ERR_NULLPTR); num_tokens >= 1 ([P3] accepts
+ * no empty tensor), d % 64 == 0 with 64 < d <= 8192, head_dim >= the row size
+ * [P3] requires (mode 1: the written bytes, 323 for d = 256; mode 0: rounded
+ * up to 32), block_stride, quant_mode in {0, 1, 2}, slot_bits (PA_ERR_INVALID);
+ * quant_mode 2 (hifloat8 / FP4) and misaligned x (PA_ERR_UNSUPPORTED).
+ * quant_group_size matters only for mode 2 (modes 0/1 use groups of 64, as
+ * [P3]'s row-size formula does); x_scale only for mode 2.
+ */
+pa_status_t pa_fp8_kv_compress_epilog_workspace_size(int num_tokens, int d, int block_num, int block_size,
+                                                     int head_dim, int64_t block_stride, int quant_group_size,
+                                                     int quant_mode, size_t* bytes_host);
+pa_status_t pa_fp8_kv_compress_epilog(uint8_t* cache_dev, const void* x_dev, const void* slot_mapping_dev,
+                                      int num_tokens, int d, int block_num, int block_size, int head_dim,
+                                      int64_t block_stride, int slot_bits, int quant_group_size, int quant_mode,
+                                      int round_scale, float x_scale, void* workspace_dev, size_t workspace_bytes,
+                                      void* stream);
 
 /* Message of the last failed call on this host thread ("" if none). */
 const char* pa_fp8_last_error(void);

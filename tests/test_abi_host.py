@@ -99,3 +99,34 @@ def scatter(lib, **over):
 def test_scatter_host_validation_codes(lib, over, code):
     assert scatter(lib, **over) == code
     assert len(lib.pa_fp8_last_error()) > 0
+
+
+def epilog(lib, **over):
+    a = dict(cache=ALIGNED, x=ALIGNED, slots=ALIGNED, T=1024, d=256, nb=128, bs=16, hd=384, bstride=16 * 384,
+             bits=32, gs=64, mode=1, rs=1, xs=1.0, stream=None)
+    a.update(over)
+    return lib.pa_fp8_kv_compress_epilog(a["cache"], a["x"], a["slots"], a["T"], a["d"], a["nb"], a["bs"], a["hd"],
+                                         a["bstride"], a["bits"], a["gs"], a["mode"], a["rs"], a["xs"], None, 0,
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(cache=None), 1), (dict(x=None), 1), (dict(slots=None), 1),
+    (dict(T=0), 2), (dict(d=200), 2), (dict(d=64), 2), (dict(d=8256), 2), (dict(hd=322), 2),
+    (dict(mode=0, hd=326), 2), (dict(mode=3), 2), (dict(bits=8), 2), (dict(bstride=100), 2),
+    (dict(mode=2, gs=8), 2), (dict(mode=2), 3), (dict(x=ctypes.c_void_p(0x10008)), 3),
+])
+def test_epilog_host_validation_codes(lib, over, code):
+    assert epilog(lib, **over) == code
+    assert len(lib.pa_fp8_last_error()) > 0
+
+
+def test_epilog_page_row_sizes_accepted(lib):
+    """The page's worked values: head_dim 323 (d = 256) and 583 (d = 512) are
+    exactly enough in mode 1, one byte less is rejected."""
+    n = ctypes.c_size_t(7)
+    for d, col in ((256, 323), (512, 583)):
+        assert lib.pa_fp8_kv_compress_epilog_workspace_size(4, d, 2, 16, col, 16 * col, 64, 1, ctypes.byref(n)) == 0
+        assert n.value == 0
+        assert lib.pa_fp8_kv_compress_epilog_workspace_size(4, d, 2, 16, col - 1, 16 * col, 64, 1,
+                                                            ctypes.byref(n)) == 2
