@@ -48,9 +48,9 @@ def lib():
         L.oracle_bf16_decode.restype = ctypes.c_double
         L.oracle_mla_dequant_row.argtypes = [P, P]
         L.oracle_mla_dequant_row.restype = None
-        L.oracle_pa_fp8_decode.argtypes = [P] * 8 + [I] * 6 + [ctypes.c_double] + [I] * 5 + [P] * 6
+        L.oracle_pa_fp8_decode.argtypes = [P] * 8 + [I] * 6 + [ctypes.c_double] + [I] * 6 + [P] * 6
         L.oracle_pa_fp8_decode.restype = I
-        L.oracle_pa_fp8_decode_rows.argtypes = ([P] * 8 + [I] * 6 + [ctypes.c_double] + [I] * 3
+        L.oracle_pa_fp8_decode_rows.argtypes = ([P] * 8 + [I] * 6 + [ctypes.c_double] + [I] * 4
                                                 + [P, I] + [P] * 4)
         L.oracle_pa_fp8_decode_rows.restype = I
         L.oracle_mla_sparse_decode.argtypes = [P] * 6 + [I] * 7 + [ctypes.c_double] + [I] * 3 + [P] * 2
@@ -121,6 +121,7 @@ def _gqa_arrays(inp):
         B=cfg.B, s1=cfg.s1, nq=cfg.nq, nkv=cfg.nkv, D=cfg.D, bs=cfg.block_size,
         scale=float(inp["softmax_scale"]), s2_tile=int(inp.get("s2_tile", cfg.s2_tile)),
         max_blocks=int(inp["block_table"].shape[1]), num_blocks=int(inp["k_cache"].shape[0]),
+        causal=1 if inp.get("causal", False) else 0,
     )
 
 
@@ -142,7 +143,7 @@ def gqa_decode(inp, threads: int = None, b_range=None) -> dict:
         rc = L.oracle_pa_fp8_decode(
             _ptr(a["q"]), _ptr(a["q_scale"]), _ptr(a["k"]), _ptr(a["ks"]), _ptr(a["v"]), _ptr(a["vs"]),
             _ptr(a["table"]), _ptr(a["seqs"]), B, s1, nq, a["nkv"], D, a["bs"], a["scale"],
-            a["s2_tile"], a["max_blocks"], a["num_blocks"], rng[0], rng[1],
+            a["s2_tile"], a["max_blocks"], a["num_blocks"], a["causal"], rng[0], rng[1],
             _ptr(out), _ptr(out_bf), _ptr(q8), _ptr(M), _ptr(Ls), _ptr(rows))
         if rc != 0:
             raise ValueError(f"oracle_pa_fp8_decode rc={rc}")
@@ -176,7 +177,7 @@ def gqa_decode_rows(inp, rows, threads: int = None) -> dict:
         rc = L.oracle_pa_fp8_decode_rows(
             _ptr(a["q"]), _ptr(a["q_scale"]), _ptr(a["k"]), _ptr(a["ks"]), _ptr(a["v"]), _ptr(a["vs"]),
             _ptr(a["table"]), _ptr(a["seqs"]), a["B"], a["s1"], a["nq"], a["nkv"], D, a["bs"], a["scale"],
-            a["s2_tile"], a["max_blocks"], a["num_blocks"], _ptr(sub), i1 - i0,
+            a["s2_tile"], a["max_blocks"], a["num_blocks"], a["causal"], _ptr(sub), i1 - i0,
             _ptr(o), _ptr(ob), _ptr(m), _ptr(l))
         if rc != 0:
             raise ValueError(f"oracle_pa_fp8_decode_rows rc={rc}")

@@ -73,7 +73,12 @@
  *  R-p   P quant: a = max P over the tile's valid tokens, ps = a / 448,
  *        code = E4M3(fp32(P / ps)); the running sum uses unquantised P.
  *  R-g   query head qh = h * G + g serves KV head h (contiguous groups).
- *  R-s1  every one of the s1 query positions attends to all of [0, seq).
+ *  R-s1  every one of the s1 query positions attends to all of [0, seq),
+ *        unless the causal variant is asked for (R-causal).
+ *  R-causal causal multi-token decode: query position s of s1 attends to the
+ *        first n_s = clamp(seq - s1 + 1 + s, 0, seq) tokens -- [P2]'s valid
+ *        count with the sequence in place of topk (section 关键实现细节) --
+ *        with its own tiles over [0, n_s) (n_s = 0 gives a zero row).
  *  R-lay the cache writer serves two layouts: BSND [block, offset, head, d]
  *        with scales [block, offset, head] -- [P1]'s layout, the one the
  *        decode reads -- and BNBD [block, head, offset, d] with scales
@@ -191,6 +196,14 @@ static int clamp_seq(int seq, int cap)
     return seq;
 }
 
+/* Tokens query position s attends to (R-s1, R-causal). */
+static int row_seq(int seq, int s1, int s, int causal)
+{
+    if (!causal) return seq;
+    int n = seq - s1 + 1 + s;
+    return n < 0 ? 0 : (n > seq ? seq : n);
+}
+
 /* Physical slot of logical token p of batch b ([P1] KV assembly, R-ids). */
 static int64_t gqa_slot(const int32_t* block_table, int max_blocks, int block_size,
                         int num_blocks, int b, int p)
@@ -297,7 +310,7 @@ static void gqa_row(const uint16_t* q_bf16, const float* q_scale,
 }
 
 /*
- * Decode batches [b_lo, b_hi).  Layouts (all dense, row-major):
+ * Decode batches [b_lo, b_hi) (causal != 0: R-causal).  Layouts (all dense, row-major):
  *   q_bf16      [B*s1, nq, D]              bf16 bit patterns
  *   q_scale     [B*s1, nq]
  *   k8, v8      [num_blocks, block_size, nkv, D]  E4M3 codes
@@ -320,7 +333,7 @@ int oracle_pa_fp8_decode(const uint16_t* q_bf16, const float* q_scale,
                          const int32_t* block_table, const int32_t* seqs,
                          int B, int s1, int nq, int nkv, int D, int block_size,
                          double softmax_scale, int s2_tile, int max_blocks, int num_blocks,
-                         int b_lo, int b_hi,
+                         int causal, int b_lo, int b_hi,
                          double* out_f64, uint16_t* out_bf16, uint8_t* q8_out,
                          double* M_out, double* L_out, int32_t* rows_out)
 {
@@ -352,7 +365,7 @@ int oracle_pa_fp8_decode(const uint16_t* q_bf16, const float* q_scale,
                     const int64_t qrow = ((int64_t)b * s1 + s) * nq + h * G + g;
                     double M, L;
                     gqa_row(q_bf16, q_scale, k8, k_scale, v8, v_scale, block_table,
-                            b, s, h, g, seq, s1, nq, nkv, D, block_size, softmax_scale,
+                            b, s, h, g, row_seq(seq, s1, s, causal), s1, nq, nkv, D, block_size, softmax_scale,
                             s2_tile, max_blocks, num_blocks,
                             out_f64 + qrow * D, q8, &M, &L, S, P, P8, O, Oraw);
                     if (q8_out) memcpy(q8_out + qrow * D, q8, D);
@@ -378,7 +391,7 @@ int oracle_pa_fp8_decode_rows(const uint16_t* q_bf16, const float* q_scale,
                               const int32_t* block_table, const int32_t* seqs,
                               int B, int s1, int nq, int nkv, int D, int block_size,
                               double softmax_scale, int s2_tile, int max_blocks, int num_blocks,
-                              const int64_t* rows, int nrows,
+                              int causal, const int64_t* rows, int nrows,
                               double* out_f64, uint16_t* out_bf16, double* M_out, double* L_out)
 {
     if (B <= 0 || s1 <= 0 || nq <= 0 || nkv <= 0 || D <= 0 || block_size <= 0 ||
@@ -405,7 +418,7 @@ int oracle_pa_fp8_decode_rows(const uint16_t* q_bf16, const float* q_scale,
         const int seq = clamp_seq(seqs[b], max_blocks * block_size);
         double M, L;
         gqa_row(q_bf16, q_scale, k8, k_scale, v8, v_scale, block_table,
-                b, s, qh / G, qh % G, seq, s1, nq, nkv, D, block_size, softmax_scale,
+                b, s, qh / G, qh % G, row_seq(seq, s1, s, causal), s1, nq, nkv, D, block_size, softmax_scale,
                 s2_tile, max_blocks, num_blocks,
                 out_f64 + (int64_t)i * D, q8, &M, &L, S, P, P8, O, Oraw);
         if (out_bf16)

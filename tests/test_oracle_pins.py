@@ -442,3 +442,44 @@ def test_mla_kv_split_planes_follow_the_row_layout():
                           cache[:, lo:hi])
     lo, hi = lay["scales_fp32"]
     assert np.array_equal(sp["kn_scales"].numpy().view(np.uint8).reshape(cache.shape[0], -1), cache[:, lo:hi])
+
+
+# ------------------------------------------------------- causal multi-token
+
+def _causal_inp(seq_lens, s1, s2_tile=256, seed=31):
+    cfg = small_cfg(B=len(seq_lens), s1=s1, nq=8, nkv=2, seq_lens=tuple(seq_lens), s2_tile=s2_tile,
+                    num_blocks=6 * len(seq_lens) + 4, max_blocks_per_seq=6, seed=seed)
+    return synth.make_gqa_inputs(cfg)
+
+
+def test_causal_row_is_the_plain_decode_of_its_prefix(oracle_mod):
+    """Position s of s1 is token seq - s1 + s of its sequence and sees tokens up to
+    itself: its causal output equals the plain single-position decode of the
+    same query over the first seq - s1 + 1 + s tokens, bit for bit."""
+    s1 = 3
+    inp = _causal_inp((300, 257, 2), s1)
+    causal = oracle_mod.gqa_decode(dict(inp, causal=True))["out_bf16"]
+    cfg = inp["cfg"]
+    for b, seq in enumerate(cfg.seq_lens):
+        for s in range(s1):
+            n = max(0, seq - s1 + 1 + s)
+            one = dict(inp, cfg=replace(cfg, B=1, s1=1, seq_lens=(n,)),
+                       q=inp["q"][b * s1 + s:b * s1 + s + 1], q_scale=inp["q_scale"][b * s1 + s:b * s1 + s + 1],
+                       block_table=inp["block_table"][b:b + 1], kv_act_seqs=torch.tensor([n], dtype=torch.int32),
+                       v_scale=inp["v_scale"][b:b + 1])
+            plain = oracle_mod.gqa_decode(one)["out_bf16"]
+            assert np.array_equal(causal[b * s1 + s], plain[0]), (b, s, n)
+
+
+def test_causal_with_one_position_is_the_plain_decode(oracle_mod):
+    inp = _causal_inp((300, 513), 1)
+    assert np.array_equal(oracle_mod.gqa_decode(dict(inp, causal=True))["out_bf16"],
+                          oracle_mod.gqa_decode(inp)["out_bf16"])
+
+
+def test_causal_positions_before_the_sequence_are_zero(oracle_mod):
+    # seq = 2 with s1 = 4: positions 0 and 1 precede the sequence (n = -1, 0)
+    inp = _causal_inp((2, 130), 4)
+    out = oracle_mod.gqa_decode(dict(inp, causal=True))["out"]
+    assert not out[0].any() and not out[1].any()
+    assert np.abs(out[2]).sum() > 0 and np.abs(out[3]).sum() > 0
