@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("PA_FP8_LIB") or os.path.join(PKG, "libpa_fp8.so")
 
 PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
 
-EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug",
+EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug", "pa_fp8_decode_causal",
            "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode",
            "pa_fp8_mla_sparse_decode_kv_split", "pa_fp8_scatter_kv_cache",
            "pa_fp8_kv_compress_epilog_workspace_size", "pa_fp8_kv_compress_epilog",
@@ -47,6 +47,8 @@ def lib():
         gqa = [P] * 9 + [I] * 6 + [F] + [I] * 4 + [P, Z]
         L.pa_fp8_decode.argtypes = gqa + [P]
         L.pa_fp8_decode.restype = I
+        L.pa_fp8_decode_causal.argtypes = [P] * 9 + [I] * 6 + [F] + [I] * 3 + [P, Z, P]
+        L.pa_fp8_decode_causal.restype = I
         L.pa_fp8_decode_debug.argtypes = gqa + [P, P, P]
         L.pa_fp8_decode_debug.restype = I
         L.pa_fp8_decode_workspace_size.argtypes = [I] * 9 + [P, P]
@@ -117,8 +119,9 @@ def _checked_inputs(ts):
 
 
 def decode(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_seqs, softmax_scale,
-           s2_tile, num_splits=0, out=None, workspace=None, stream=None, s1=None):
-    """FP8 paged decode; returns out [B*s1, nq, D] bf16 (allocated if not given)."""
+           s2_tile, num_splits=0, out=None, workspace=None, stream=None, s1=None, causal=False):
+    """FP8 paged decode; returns out [B*s1, nq, D] bf16 (allocated if not given).
+    causal=True: pa_fp8_decode_causal (position s of s1 sees the first seq - s1 + 1 + s tokens)."""
     B, s1, nq, nkv, D, bs, nblk, mbps = _shapes(q, k_cache, block_table, kv_act_seqs, s1)
     _checked_inputs(dict(q=q, q_scale=q_scale, k_cache=k_cache, k_scale=k_scale, v_cache=v_cache,
                          v_scale=v_scale, block_table=block_table, kv_act_seqs=kv_act_seqs, out=out,
@@ -129,6 +132,14 @@ def decode(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_s
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if causal:
+        if num_splits:
+            raise ValueError("causal decode takes num_splits = 0")
+        _check(lib().pa_fp8_decode_causal(
+            _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+            _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),
+            int(s2_tile), mbps, nblk, _ptr(workspace), wbytes, _stream(stream)))
+        return out
     _check(lib().pa_fp8_decode(
         _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
         _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),
@@ -155,11 +166,12 @@ def decode_debug(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv
 
 
 def decode_inputs(inp: dict, num_splits=0, out=None, workspace=None, stream=None):
-    """decode() on a dict produced by fp8_paged_kv_amd.synth.make_gqa_inputs."""
+    """decode() on a dict produced by fp8_paged_kv_amd.synth.make_gqa_inputs (inp["causal"] selects
+    the causal variant)."""
     return decode(inp["q"], inp["q_scale"], inp["k_cache"], inp["k_scale"], inp["v_cache"], inp["v_scale"],
                   inp["block_table"], inp["kv_act_seqs"], inp["softmax_scale"],
                   inp.get("s2_tile", inp["cfg"].s2_tile), num_splits=num_splits, out=out, workspace=workspace,
-                  stream=stream, s1=inp["cfg"].s1)
+                  stream=stream, s1=inp["cfg"].s1, causal=bool(inp.get("causal", False)))
 
 
 def mla_workspace_size(B, s1, nq, topk, s2_tile):

@@ -128,7 +128,7 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
                 const int32_t* seqs, void* out, int B, int s1, int nq, int nkv, int D, int block_size,
                 float softmax_scale, int s2_tile, int max_blocks, int num_blocks, int num_splits,
                 void* workspace, size_t workspace_bytes, int32_t* rows_dev, uint8_t* q8_dev,
-                bool debug, void* stream) {
+                bool debug, bool causal, void* stream) {
     g_err[0] = 0;
     if (!q || !q_scale || !k_cache || !k_scale || !v_cache || !v_scale || !block_table || !seqs || !out)
         return fail(PA_ERR_NULLPTR, "a required tensor pointer is NULL");
@@ -143,6 +143,9 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     const int capacity = max_blocks * block_size;
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
     const bool rows = use_rows_path(B, s1, nq, nkv, s2_tile, num_splits);
+    if (causal && !rows)
+        return fail(PA_ERR_UNSUPPORTED, "causal decode runs on the whole-row path only: num_splits must be 0, "
+                    "at most 32 query rows per KV head, s2_tile 128-1024");
     const int nsplit = rows ? 1 : plan_splits(B, nkv, max_tiles, num_splits);
     const int tps = (max_tiles + nsplit - 1) / nsplit;
     const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit, rows, max_tiles);
@@ -191,6 +194,7 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.nsplit_pad = nsplit_pad;
     p.tiles_per_split = tps;
     p.softmax_scale = softmax_scale;
+    p.causal = causal ? 1 : 0;
 
     hipError_t e;
     if (rows) {
@@ -298,7 +302,7 @@ pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev, const uin
     return run(q_dev, q_scale_dev, k_cache_dev, k_scale_dev, v_cache_dev, v_scale_dev, block_table_dev,
                kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
                max_blocks_per_seq, num_blocks, num_splits, workspace_dev, workspace_bytes, nullptr, nullptr,
-               false, stream);
+               false, false, stream);
 }
 
 pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
@@ -311,7 +315,19 @@ pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev, con
     return run(q_dev, q_scale_dev, k_cache_dev, k_scale_dev, v_cache_dev, v_scale_dev, block_table_dev,
                kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
                max_blocks_per_seq, num_blocks, num_splits, workspace_dev, workspace_bytes, rows_dev, q8_dev,
-               true, stream);
+               true, false, stream);
+}
+
+pa_status_t pa_fp8_decode_causal(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
+                                 const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,
+                                 const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev, void* out_dev,
+                                 int B, int s1, int nq, int nkv, int D, int block_size, float softmax_scale,
+                                 int s2_tile, int max_blocks_per_seq, int num_blocks, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream) {
+    return run(q_dev, q_scale_dev, k_cache_dev, k_scale_dev, v_cache_dev, v_scale_dev, block_table_dev,
+               kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
+               max_blocks_per_seq, num_blocks, 0, workspace_dev, workspace_bytes, nullptr, nullptr, false, true,
+               stream);
 }
 
 pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_tile, size_t* bytes_host) {

@@ -30,6 +30,7 @@ struct DecodeParams {
     int s2_tile, max_blocks, num_blocks, capacity;
     int nsplit, nsplit_pad, tiles_per_split;
     int rows_kmax;              // whole-row path: partial slots per (batch, KV head) = tiles
+    int causal;                 // whole-row path: position s of s1 sees the first seq - s1 + 1 + s tokens
     float softmax_scale;
 };
 

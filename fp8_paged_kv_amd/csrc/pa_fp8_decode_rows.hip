@@ -326,6 +326,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     // ---- running state of this wave (head hl, token half p) -----------------------------------
     bf16x8 qop[NRB][4];
     float qcoef[NRB];
+    int lim[NRB];                            // tokens this lane's query row attends to (causal: fewer)
+    int mlim = 0;                            // the smallest of them over the rows
     float M_s[NRB], L_s[NRB], M_o[NRB][4];
     f32x4 O[NRB][8];
     int seg_t0 = 0;                          // first tile of the current segment
@@ -391,6 +393,9 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                         const int rr = rb * 16 + lr;
                         uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                         qcoef[rb] = 0.f;
+                        // causal decode: position s of s1 attends to the first seq - s1 + 1 + s tokens
+                        lim[rb] = cur.seq - (a.causal ? a.s1 - 1 - (rr < rows ? rr / a.G : a.s1 - 1) : 0);
+                        mlim = cur.seq - (a.causal ? a.s1 - 1 : 0);
                         if (rr < rows) {
                             const int sr = hl * rows + rr;
                             const float qs = s_qs[vs_buf][sr];
@@ -459,12 +464,12 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 #pragma unroll
                             for (int i = 0; i < 4; ++i) sv[rb][q][4 * k + i] = acc[rb][i] * kk[i] * qcoef[rb];
                     }
-                    if (p0 + 32 > cur.seq) {
+                    if (p0 + 32 > mlim) {
 #pragma unroll
                         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
                             for (int j = 0; j < 8; ++j)
-                                sv[rb][q][j] = (p0 + chunk_token(lg, j) < cur.seq) ? sv[rb][q][j] : -INFINITY;
+                                sv[rb][q][j] = (p0 + chunk_token(lg, j) < lim[rb]) ? sv[rb][q][j] : -INFINITY;
                     }
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
@@ -501,8 +506,9 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                     for (int rb = 0; rb < NRB; ++rb) {
                         const float m = fmaxf(mown[rb], s_max[w ^ 1][rb * 16 + lr]);
                         mt_s[rb] = m;
-                        // P' = 448 exp2(S - m_tile) = exp2(S + off); a dropped row gets off = -inf
-                        const float poff = (M_s[rb] - m > kDropLog2) ? -INFINITY : kLog2_448 - m;
+                        // P' = 448 exp2(S - m_tile) = exp2(S + off); a dropped row, or one with no
+                        // token in this tile (causal), gets off = -inf
+                        const float poff = (m == -INFINITY || M_s[rb] - m > kDropLog2) ? -INFINITY : kLog2_448 - m;
                         // steps 5b-6 for this half of the tile: the FP8 code of P' (the tile's
                         // max maps to 448) and the running sum of the unquantised P'
 #pragma unroll
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                             const float mo = __shfl(m, 4 * lg + i, 64);
                             mt_o[rb][i] = mo;
                             const float d = M_o[rb][i] - mo;
-                            const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(d);
+                            const float sc = (mo == -INFINITY || d > kDropLog2) ? 1.f : __builtin_amdgcn_exp2f(d);
 #pragma unroll
                             for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
                         }
@@ -569,14 +575,17 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         // ---- steps 8-9: finish the rescale, update the running state --------------------------
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-            const float mn = fmaxf(M_s[rb], mt_s[rb]);
-            L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) + lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
-            M_s[rb] = mn;
+            // a row with no token in this tile (causal) keeps its state
+            if (mt_s[rb] != -INFINITY) {
+                const float mn = fmaxf(M_s[rb], mt_s[rb]);
+                L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) + lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
+                M_s[rb] = mn;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float mo = fmaxf(M_o[rb][i], mt_o[rb][i]);
                 const float d = M_o[rb][i] - mt_o[rb][i];
-                const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
+                const float sc = (mt_o[rb][i] == -INFINITY || d > kDropLog2) ? 1.f : __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
                 M_o[rb][i] = mo;
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
@@ -627,7 +636,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                         const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
                         if (!split) {
                             // step 10: out = O * v_scale / L' (L' = 448 L), bf16
-                            const float inv = 1.f / Lr;
+                            const float inv = Lr > 0.f ? 1.f / Lr : 0.f;     // no token at all (causal): zeros
                             uint32_t pk[4];
 #pragma unroll
                             for (int q2 = 0; q2 < 4; ++q2) {
@@ -748,7 +757,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
     }
     const int sq = rr / a.G, gq = rr - sq * a.G;
     const int64_t qrow = ((int64_t)b * a.s1 + sq) * a.nq + h * a.G + gq;
-    const float inv = 1.f / L;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
     uint32_t pk[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {

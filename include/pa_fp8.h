@@ -141,6 +141,24 @@ pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev,
                                 int32_t* rows_dev, uint8_t* q8_dev, void* stream);
 
 /*
+ * Causal multi-token decode: pa_fp8_decode with query position s of s1
+ * attending to the first n_s = clamp(seq - s1 + 1 + s, 0, seq) tokens only
+ * (the s1 new tokens are the sequence's last ones and each sees itself and
+ * what precedes it) -- [P2]'s valid count (section 关键实现细节) with the
+ * sequence in place of topk.  Each position keeps its own tiles over [0, n_s)
+ * (P quantised per row over the tile's tokens that row sees); n_s = 0 gives a
+ * zero row.  Same arguments and workspace as pa_fp8_decode with
+ * num_splits = 0; shapes outside the whole-row path (more than 32 query rows
+ * per KV head, s2_tile 2048, very large batches) return PA_ERR_UNSUPPORTED.
+ */
+pa_status_t pa_fp8_decode_causal(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
+                                 const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,
+                                 const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev, void* out_dev,
+                                 int B, int s1, int nq, int nkv, int D, int block_size, float softmax_scale,
+                                 int s2_tile, int max_blocks_per_seq, int num_blocks, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Workspace bytes pa_fp8_mla_sparse_decode needs for these sizes.
  */
 pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_tile, size_t* bytes_host);

@@ -130,3 +130,10 @@ def test_epilog_page_row_sizes_accepted(lib):
         assert n.value == 0
         assert lib.pa_fp8_kv_compress_epilog_workspace_size(4, d, 2, 16, col - 1, 16 * col, 64, 1,
                                                             ctypes.byref(n)) == 2
+
+
+def test_causal_needs_the_whole_row_path(lib):
+    """More than 32 query rows per KV head (s1=2, G=32) is outside the whole-row path."""
+    rc = lib.pa_fp8_decode_causal(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 2, 128, 128,
+                                  0.088, 256, 6, 8, FAKE, 1 << 20, None)
+    assert rc == 3 and b"whole-row" in lib.pa_fp8_last_error()

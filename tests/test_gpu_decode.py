@@ -191,3 +191,35 @@ def test_shared_workspace_between_paths(B, oracle_mod):
         out = B.decode_inputs(d, num_splits=ns, workspace=ws)
         torch.cuda.synchronize()
         compare(gpu_out_float(out), ref["out_bf16"], f"shared workspace call {i} splits={ns}")
+
+
+@pytest.mark.parametrize("s1,nq,nkv,s2_tile,seqs", [
+    (4, 32, 4, 256, (1, 3, 4, 5, 257, 258, 515, 1024)),     # seq < s1, last tiles with fewer tokens than s1
+    (2, 48, 8, 512, (700, 1, 513, 2049)),
+    (3, 30, 3, 128, (130, 129, 3, 384)),                     # odd KV heads (one head per workgroup)
+    (1, 96, 8, 512, (900, 4000)),                            # s1 = 1: the plain decode
+])
+def test_causal_parity(B, oracle_mod, s1, nq, nkv, s2_tile, seqs):
+    mb = (max(seqs) + 127) // 128 + 1
+    cfg = _case(f"causal-s1{s1}", B=len(seqs), s1=s1, nq=nq, nkv=nkv, s2_tile=s2_tile, seq_lens=seqs,
+                num_blocks=mb * len(seqs), max_blocks_per_seq=mb, seed=40 + s1)
+    inp = dict(synth.make_gqa_inputs(cfg), causal=True)
+    ref = oracle_mod.gqa_decode(inp)
+    got = _run(B, inp, 0, "causal")
+    compare(got, ref["out_bf16"], f"causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile}")
+    if s1 == 1:
+        assert np.array_equal(got, _run(B, dict(inp, causal=False), 0, "plain"))
+
+
+def test_causal_full_size_config3_sampled_rows(B, oracle_mod):
+    """The multi-token workload (B=256, s1=4, nq=32, nkv=4) decoded causally."""
+    cfg = synth.CONFIGS[3]
+    print("[gpu] causal config 3 generating on GPU", flush=True)
+    inp_d = dict(synth.make_gqa_inputs(cfg, device="cuda"), causal=True)
+    out = _run_dev(B, inp_d, "config3-causal")
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp_d.items()}
+    nrows = cfg.B * cfg.s1 * cfg.nq
+    g = np.random.default_rng(33)
+    rows = np.unique(np.concatenate([[0, nrows - 1], g.choice(nrows, 62, replace=False)]))
+    ref = oracle_mod.gqa_decode_rows(host, rows)
+    compare(out.reshape(nrows, cfg.D)[rows], ref["out_bf16"], "config3 causal sampled rows")
