@@ -13,13 +13,16 @@
 // divided by the sum (section 在线反量化与 Online Softmax).
 //
 // Work: one workgroup per (query token, tile, block of 32 query heads); four
-// waves.  Wave w computes the scores of rows [w T/4, (w+1) T/4) of the tile for
-// the 32 heads, gathering and dequantising K straight into MFMA operands
-// (16x16x32 bf16, products exact, FP32 accumulation).  The waves exchange row
-// maxima and sums through LDS and publish BF16 P in LDS; then wave w computes
-// P.V for output channels [128 w, 128 w + 128) over all rows of the tile,
-// dequantising V rows on the fly (an 8x8 byte transpose turns row-major codes
-// into MFMA operands).  Each (token, head, tile) leaves an (O, m, l) partial;
+// waves.  Q of the 32 heads sits in LDS, already in MFMA B-operand order.  Wave
+// w computes the scores of rows [w T/4, (w+1) T/4) of the tile for the 32
+// heads, 16 rows at a time, gathering and dequantising K straight into MFMA
+// operands (16x16x32 bf16, products exact, FP32 accumulation); the K rows of
+// the next groups are requested before the current one is multiplied.  The
+// waves exchange row maxima and sums through LDS and publish BF16 P in LDS;
+// then wave w computes P.V for output channels [128 w, 128 w + 128) over all
+// rows of the tile, dequantising V rows on the fly (an 8x8 byte transpose
+// turns row-major codes into MFMA operands), again with the next blocks'
+// rows in flight.  Each (token, head, tile) leaves an (O, m, l) partial;
 // mla_merge_kernel combines the tiles of each (token, head).
 //
 // The rows are addressed as three planes (nope codes, rope values, group
@@ -67,6 +70,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
     __shared__ int s_row[T];                                   // cache row of each tile position, -1 = past n
     __shared__ __attribute__((aligned(16))) uint8_t s_p[NB][2][64 * 16];   // BF16 P, MFMA A-operand layout
     __shared__ float s_max[4][kMlaHeads], s_sum[4][kMlaHeads];
+    __shared__ __attribute__((aligned(16))) uint8_t s_qop[2][18][64 * 16];  // Q as MFMA B operands, per lane
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -111,72 +115,71 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
     // MFMA ks (0..15) takes nope channels 64 (ks / 2) + 16 g + 8 (ks % 2) + [0, 8);
     // ks 16, 17 take rope channels 16 g + 8 (ks - 16) + [0, 8).
     const int h0 = hb * kMlaHeads;
-    bf16x8 qop[2][18];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int pq = w; pq < 36; pq += 4) {                     // (head half, k-slot) pairs over the waves
+        const int hh = pq / 18, ks = pq - 18 * (pq / 18);
         const int64_t qrow = (int64_t)bs * a.nq + h0 + 16 * hh + lr;
-        const uint16_t* qn = a.q_nope + qrow * kMlaNope;
-        const uint16_t* qr = a.q_rope + qrow * kMlaRope;
-#pragma unroll
-        for (int pr = 0; pr < 8; ++pr) {
-            const i32x4 x0 = *reinterpret_cast<const i32x4*>(qn + 64 * pr + 16 * lg);
-            const i32x4 x1 = *reinterpret_cast<const i32x4*>(qn + 64 * pr + 16 * lg + 8);
-            qop[hh][2 * pr] = __builtin_bit_cast(bf16x8, x0);
-            qop[hh][2 * pr + 1] = __builtin_bit_cast(bf16x8, x1);
-        }
-        const i32x4 r0 = *reinterpret_cast<const i32x4*>(qr + 16 * lg);
-        const i32x4 r1 = *reinterpret_cast<const i32x4*>(qr + 16 * lg + 8);
-        qop[hh][16] = __builtin_bit_cast(bf16x8, r0);
-        qop[hh][17] = __builtin_bit_cast(bf16x8, r1);
+        const uint16_t* src = ks < 16 ? a.q_nope + qrow * kMlaNope + 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1)
+                                      : a.q_rope + qrow * kMlaRope + 16 * lg + 8 * (ks - 16);
+        *reinterpret_cast<i32x4*>(&s_qop[hh][ks][16 * lane]) = *reinterpret_cast<const i32x4*>(src);
     }
     __syncthreads();
+    auto qop = [&](int hh, int ks) { return *reinterpret_cast<const bf16x8*>(&s_qop[hh][ks][16 * lane]); };
 
     // ---- scores of this wave's rows: S^T (rows x heads), log2 units ------------------------
     const float coef = a.softmax_scale * kLog2e;
     float sv[2][NCH][8];
     float rmax[2] = {-INFINITY, -INFINITY};
+    // K rows of 16-row group gq + 3 are requested while group gq is multiplied
+    constexpr int NGQ = 2 * NCH;                          // 16-row groups of this wave
+    struct KRows { f32x4 gs; i32x4 x[8]; i32x4 r0, r1; };
+    KRows kq[3];
+    auto issue_k = [&](int gq, KRows& kr) {
+        const int row = s_row[w * RW + 16 * gq + lr];     // this lane's K row (A operand row lr)
+        const int64_t r = row < 0 ? 0 : row;
+        const uint8_t* rp = a.nope + r * a.nope_stride;
+        const uint8_t* rrp = a.rope + r * a.rope_stride;
+        kr.gs = *reinterpret_cast<const f32x4*>(a.scales + r * a.scale_stride);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+        for (int pr = 0; pr < 8; ++pr) kr.x[pr] = *reinterpret_cast<const i32x4*>(rp + 64 * pr + 16 * lg);
+        kr.r0 = *reinterpret_cast<const i32x4*>(rrp + 32 * lg);
+        kr.r1 = *reinterpret_cast<const i32x4*>(rrp + 32 * lg + 16);
+    };
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int li = w * RW + 32 * c + 16 * k + lr;     // this lane's K row (A operand row lr)
-            const int row = s_row[li];
-            const int64_t r = row < 0 ? 0 : row;
-            const uint8_t* rp = a.nope + r * a.nope_stride;
-            const uint8_t* rr = a.rope + r * a.rope_stride;
-            const f32x4 gs = *reinterpret_cast<const f32x4*>(a.scales + r * a.scale_stride);
-            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int i = 0; i < 3; ++i)
+        if (i < NGQ) issue_k(i, kq[i]);
 #pragma unroll
-            for (int pr = 0; pr < 8; ++pr) {
-                const i32x4 x = *reinterpret_cast<const i32x4*>(rp + 64 * pr + 16 * lg);
-                const float g = gs[pr >> 1];
-                const float sc[8] = {g, g, g, g, g, g, g, g};
-                const bf16x8 k0 = dequant8((uint32_t)x[0], (uint32_t)x[1], sc);
-                const bf16x8 k1 = dequant8((uint32_t)x[2], (uint32_t)x[3], sc);
+    for (int gq = 0; gq < NGQ; ++gq) {
+        const int c = gq >> 1, k = gq & 1;
+        KRows& kr = kq[gq % 3];
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    acc[hh] = mfma_bf16(k0, qop[hh][2 * pr], acc[hh]);
-                    acc[hh] = mfma_bf16(k1, qop[hh][2 * pr + 1], acc[hh]);
-                }
-            }
-            const i32x4 r0 = *reinterpret_cast<const i32x4*>(rr + 32 * lg);
-            const i32x4 r1 = *reinterpret_cast<const i32x4*>(rr + 32 * lg + 16);
+        for (int pr = 0; pr < 8; ++pr) {
+            const float g = kr.gs[pr >> 1];
+            const float sc[8] = {g, g, g, g, g, g, g, g};
+            const bf16x8 k0 = dequant8((uint32_t)kr.x[pr][0], (uint32_t)kr.x[pr][1], sc);
+            const bf16x8 k1 = dequant8((uint32_t)kr.x[pr][2], (uint32_t)kr.x[pr][3], sc);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                acc[hh] = mfma_bf16(__builtin_bit_cast(bf16x8, r0), qop[hh][16], acc[hh]);
-                acc[hh] = mfma_bf16(__builtin_bit_cast(bf16x8, r1), qop[hh][17], acc[hh]);
+                acc[hh] = mfma_bf16(k0, qop(hh, 2 * pr), acc[hh]);
+                acc[hh] = mfma_bf16(k1, qop(hh, 2 * pr + 1), acc[hh]);
             }
-            // lane (head lr, group lg) holds rows 16 k + 4 lg + i of this 32-row chunk
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ok = s_row[w * RW + 32 * c + 16 * k + 4 * lg + i] >= 0;
-                    const float x = ok ? acc[hh][i] * coef : -INFINITY;
-                    sv[hh][c][4 * k + i] = x;
-                    rmax[hh] = fmaxf(rmax[hh], x);
-                }
         }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            acc[hh] = mfma_bf16(__builtin_bit_cast(bf16x8, kr.r0), qop(hh, 16), acc[hh]);
+            acc[hh] = mfma_bf16(__builtin_bit_cast(bf16x8, kr.r1), qop(hh, 17), acc[hh]);
+        }
+        if (gq + 3 < NGQ) issue_k(gq + 3, kr);
+        // lane (head lr, group lg) holds rows 16 k + 4 lg + i of this 32-row chunk
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = s_row[w * RW + 32 * c + 16 * k + 4 * lg + i] >= 0;
+                const float x = ok ? acc[hh][i] * coef : -INFINITY;
+                sv[hh][c][4 * k + i] = x;
+                rmax[hh] = fmaxf(rmax[hh], x);
+            }
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -214,7 +217,28 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int c = 0; c < 8; ++c) O[hh][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the V rows of block bi + PD are requested while block bi is multiplied
+    constexpr int PD = 5;
+    uint2 xq[PD][8];
+    float sq[PD][8];
+    int negq[PD];
+    auto issue_v = [&](int bi, uint2 (&x)[8], float (&sc)[8], int& neg) {
+        neg = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = s_row[32 * bi + chunk_token(lg, j)];
+            const int64_t r = row < 0 ? 0 : row;
+            x[j] = *reinterpret_cast<const uint2*>(a.nope + r * a.nope_stride + 128 * w + 8 * lr);
+            sc[j] = *reinterpret_cast<const float*>(a.scales + r * a.scale_stride + 4 * w);
+            neg |= (row < 0) << j;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < PD; ++i)
+        if (i < NB) issue_v(i, xq[i], sq[i], negq[i]);
+#pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
+        const int q = bi % PD;
         bf16x8 pop[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) pop[hh] = *reinterpret_cast<const bf16x8*>(&s_p[bi][hh][16 * lane]);
@@ -222,14 +246,12 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
         float scj[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int row = s_row[32 * bi + chunk_token(lg, j)];
-            const int64_t r = row < 0 ? 0 : row;
-            const uint2 x = *reinterpret_cast<const uint2*>(a.nope + r * a.nope_stride + 128 * w + 8 * lr);
-            const float g = *reinterpret_cast<const float*>(a.scales + r * a.scale_stride + 4 * w);
-            xl[j] = row < 0 ? 0u : x.x;            // positions past n: zero codes (P is 0 there)
-            xh[j] = row < 0 ? 0u : x.y;
-            scj[j] = g;
+            const bool neg = (negq[q] >> j) & 1;            // positions past n: zero codes (P is 0 there)
+            xl[j] = neg ? 0u : xq[q][j].x;
+            xh[j] = neg ? 0u : xq[q][j].y;
+            scj[j] = sq[q][j];
         }
+        if (bi + PD < NB) issue_v(bi + PD, xq[q], sq[q], negq[q]);
         uint32_t ylo[8], yhi[8];
         transpose4(xl[0], xl[1], xl[2], xl[3], ylo[0], ylo[1], ylo[2], ylo[3]);
         transpose4(xl[4], xl[5], xl[6], xl[7], yhi[0], yhi[1], yhi[2], yhi[3]);
