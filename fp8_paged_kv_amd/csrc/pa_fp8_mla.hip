@@ -12,14 +12,15 @@
 // unquantised P feeds the running sum; tiles are merged online and the result
 // divided by the sum (section 在线反量化与 Online Softmax).
 //
-// Work: one workgroup per (query token, tile, block of 32 query heads); four
-// waves.  Q of the 32 heads sits in LDS, already in MFMA B-operand order.  Wave
-// w computes the scores of rows [w T/4, (w+1) T/4) of the tile for the 32
+// Work: one workgroup per (query token, tile, block of 32 query heads); eight
+// waves (four for 128-index tiles), two per SIMD.  Q of the 32 heads sits in
+// LDS, already in MFMA B-operand order.  Wave w computes the scores of its
+// T/8 rows of the tile for the 32
 // heads, 16 rows at a time, gathering and dequantising K straight into MFMA
 // operands (16x16x32 bf16, products exact, FP32 accumulation); the K rows of
 // the next groups are requested before the current one is multiplied.  The
 // waves exchange row maxima and sums through LDS and publish BF16 P in LDS;
-// then wave w computes P.V for output channels [128 w, 128 w + 128) over all
+// then wave w computes P.V for its 64 output channels over all
 // rows of the tile, dequantising V rows on the fly (an 8x8 byte transpose
 // turns row-major codes into MFMA operands), again with the next blocks'
 // rows in flight.  Each (token, head, tile) leaves an (O, m, l) partial;
@@ -60,16 +61,18 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w0, uint32_t w1, const float
     return r;
 }
 
-template <int T>
-__global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
-    constexpr int RW = T / 4;             // rows of the tile whose scores a wave computes
+template <int T, int NWV>
+__global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
+    constexpr int RW = T / NWV;           // rows of the tile whose scores a wave computes
     constexpr int NCH = RW / 32;          // 32-row chunks per wave
     constexpr int NB = T / 32;            // 32-row blocks of the tile
-    static_assert(NCH >= 1, "tile of at least 128 indices");
+    constexpr int CPW = kMlaNope / NWV;   // output channels per wave in P.V
+    constexpr int CL = CPW / 16;          // of them per lane (one MFMA each)
+    static_assert(NCH >= 1 && (CL == 8 || CL == 4), "tile of at least 32 rows per wave");
 
     __shared__ int s_row[T];                                   // cache row of each tile position, -1 = past n
     __shared__ __attribute__((aligned(16))) uint8_t s_p[NB][2][64 * 16];   // BF16 P, MFMA A-operand layout
-    __shared__ float s_max[4][kMlaHeads], s_sum[4][kMlaHeads];
+    __shared__ float s_max[NWV][kMlaHeads], s_sum[NWV][kMlaHeads];
     __shared__ __attribute__((aligned(16))) uint8_t s_qop[2][18][64 * 16];  // Q as MFMA B operands, per lane
 
     const int lane = threadIdx.x & 63;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
     if (t * T >= n) return;                                    // no such tile for this token
 
     // ---- cache rows of the tile's positions -----------------------------------------------
-    for (int i = threadIdx.x; i < T; i += 256) {
+    for (int i = threadIdx.x; i < T; i += NWV * 64) {
         const int j = t * T + i;
         int row = -1;
         if (j < n) {
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
     // MFMA ks (0..15) takes nope channels 64 (ks / 2) + 16 g + 8 (ks % 2) + [0, 8);
     // ks 16, 17 take rope channels 16 g + 8 (ks - 16) + [0, 8).
     const int h0 = hb * kMlaHeads;
-    for (int pq = w; pq < 36; pq += 4) {                     // (head half, k-slot) pairs over the waves
+    for (int pq = w; pq < 36; pq += NWV) {                     // (head half, k-slot) pairs over the waves
         const int hh = pq / 18, ks = pq - 18 * (pq / 18);
         const int64_t qrow = (int64_t)bs * a.nq + h0 + 16 * hh + lr;
         const uint16_t* src = ks < 16 ? a.q_nope + qrow * kMlaNope + 64 * (ks >> 1) + 16 * lg + 8 * (ks & 1)
@@ -193,7 +196,9 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int hc = 16 * hh + lr;
-        mt[hh] = fmaxf(fmaxf(s_max[0][hc], s_max[1][hc]), fmaxf(s_max[2][hc], s_max[3][hc]));
+        mt[hh] = s_max[0][hc];
+#pragma unroll
+        for (int i = 1; i < NWV; ++i) mt[hh] = fmaxf(mt[hh], s_max[i][hc]);
         float l = 0.f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -211,25 +216,33 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
     }
     __syncthreads();
 
-    // ---- P.V for channels [128 w, 128 w + 128): O[head][channel] -------------------------
-    f32x4 O[2][8];
+    // ---- P.V for channels [CPW w, CPW w + CPW): O[head][channel] -------------------------
+    f32x4 O[2][CL];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) O[hh][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CL; ++c) O[hh][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int grp = CPW * w / 128;                            // the channels' scale group
     // the V rows of block bi + PD are requested while block bi is multiplied
-    constexpr int PD = 5;
-    uint2 xq[PD][8];
+    constexpr int PD = CL == 8 ? 5 : 6;
+    uint32_t xq[PD][8][CL / 4];
     float sq[PD][8];
     int negq[PD];
-    auto issue_v = [&](int bi, uint2 (&x)[8], float (&sc)[8], int& neg) {
+    auto issue_v = [&](int bi, uint32_t (&x)[8][CL / 4], float (&sc)[8], int& neg) {
         neg = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int row = s_row[32 * bi + chunk_token(lg, j)];
             const int64_t r = row < 0 ? 0 : row;
-            x[j] = *reinterpret_cast<const uint2*>(a.nope + r * a.nope_stride + 128 * w + 8 * lr);
-            sc[j] = *reinterpret_cast<const float*>(a.scales + r * a.scale_stride + 4 * w);
+            const uint8_t* vp = a.nope + r * a.nope_stride + CPW * w + CL * lr;
+            if (CL == 8) {
+                const uint2 v2 = *reinterpret_cast<const uint2*>(vp);
+                x[j][0] = v2.x;
+                x[j][CL / 4 - 1] = v2.y;
+            } else {
+                x[j][0] = *reinterpret_cast<const uint32_t*>(vp);
+            }
+            sc[j] = *reinterpret_cast<const float*>(a.scales + r * a.scale_stride + 4 * grp);
             neg |= (row < 0) << j;
         }
     };
@@ -247,19 +260,21 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bool neg = (negq[q] >> j) & 1;            // positions past n: zero codes (P is 0 there)
-            xl[j] = neg ? 0u : xq[q][j].x;
-            xh[j] = neg ? 0u : xq[q][j].y;
+            xl[j] = neg ? 0u : xq[q][j][0];
+            xh[j] = neg ? 0u : xq[q][j][CL / 4 - 1];
             scj[j] = sq[q][j];
         }
         if (bi + PD < NB) issue_v(bi + PD, xq[q], sq[q], negq[q]);
         uint32_t ylo[8], yhi[8];
         transpose4(xl[0], xl[1], xl[2], xl[3], ylo[0], ylo[1], ylo[2], ylo[3]);
         transpose4(xl[4], xl[5], xl[6], xl[7], yhi[0], yhi[1], yhi[2], yhi[3]);
-        transpose4(xh[0], xh[1], xh[2], xh[3], ylo[4], ylo[5], ylo[6], ylo[7]);
-        transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
+        if (CL == 8) {
+            transpose4(xh[0], xh[1], xh[2], xh[3], ylo[4], ylo[5], ylo[6], ylo[7]);
+            transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
+        }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const bf16x8 vop = dequant8(ylo[c], yhi[c], scj);      // channel 128 w + 8 lr + c, 8 rows
+        for (int c = 0; c < CL; ++c) {
+            const bf16x8 vop = dequant8(ylo[c], yhi[c], scj);      // channel CPW w + CL lr + c, 8 rows
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) O[hh][c] = mfma_bf16(pop[hh], vop, O[hh][c]);
         }
@@ -272,15 +287,20 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(MlaParams a) {
         for (int i = 0; i < 4; ++i) {
             const int head = h0 + 16 * hh + 4 * lg + i;
             const int64_t slot = ((int64_t)bs * a.nq + head) * a.ntiles_max + t;
-            float* po = a.part_o + slot * kMlaNope + 128 * w + 8 * lr;
-            *reinterpret_cast<f32x4*>(po) = f32x4{O[hh][0][i], O[hh][1][i], O[hh][2][i], O[hh][3][i]};
-            *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[hh][4][i], O[hh][5][i], O[hh][6][i], O[hh][7][i]};
+            float* po = a.part_o + slot * kMlaNope + CPW * w + CL * lr;
+#pragma unroll
+            for (int c4 = 0; c4 < CL / 4; ++c4)
+                *reinterpret_cast<f32x4*>(po + 4 * c4) =
+                    f32x4{O[hh][4 * c4][i], O[hh][4 * c4 + 1][i], O[hh][4 * c4 + 2][i], O[hh][4 * c4 + 3][i]};
         }
         if (w == 0 && lg == 0) {
             const int hc = 16 * hh + lr;
             const int64_t slot = ((int64_t)bs * a.nq + h0 + hc) * a.ntiles_max + t;
+            float l = 0.f;
+#pragma unroll
+            for (int i = 0; i < NWV; ++i) l += s_sum[i][hc];
             a.part_ml[slot * 2] = mt[hh];
-            a.part_ml[slot * 2 + 1] = s_sum[0][hc] + s_sum[1][hc] + s_sum[2][hc] + s_sum[3][hc];
+            a.part_ml[slot * 2 + 1] = l;
         }
     }
 }
@@ -326,8 +346,9 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams a, int T) {
 
 template <int T>
 static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
+    constexpr int NWV = T >= 256 ? 8 : 4;                     // waves: at least 32 tile rows each
     const int64_t grid = (int64_t)p.B * p.s1 * p.ntiles_max * (p.nq / kMlaHeads);
-    if (grid > 0) hipLaunchKernelGGL((mla_decode_kernel<T>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    if (grid > 0) hipLaunchKernelGGL((mla_decode_kernel<T, NWV>), dim3((unsigned)grid), dim3(NWV * 64), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = (int64_t)p.B * p.s1 * p.nq;
