@@ -80,6 +80,10 @@ __device__ __forceinline__ int lds_uniform(const int* p) { return __builtin_amdg
 
 constexpr int kStepTok = 128;             // tokens per step = one cache block
 constexpr int kPrefixMax = 1024;          // (batch, head group) pairs of one call
+// Cost of starting a (batch, group) sequence in a workgroup (staging and converting its
+// query rows, and finishing its output), in steps: measured at about four steps.  The
+// partition charges it to the sequence's first tile.
+constexpr int kSegW = 4;
 
 template <int NRB, int NBLK, int HG, bool DBG>
 __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a) {
@@ -131,7 +135,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         int cost = 0, units = 0;
         for (int v = v0; v < v1; ++v) {
             const int s = s_seq[v / NG];
-            cost += 2 * ((s + kStepTok - 1) / kStepTok);
+            const int nb = (s + kStepTok - 1) / kStepTok;
+            cost += 2 * nb + (nb > 0 ? kSegW : 0);
             units += (s + T - 1) / T;
         }
         int incl = cost;
@@ -143,7 +148,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         int run = incl - cost;
         for (int v = v0; v < v1; ++v) {
             s_pref[v] = run;
-            run += 2 * ((s_seq[v / NG] + kStepTok - 1) / kStepTok);
+            const int nb = (s_seq[v / NG] + kStepTok - 1) / kStepTok;
+            run += 2 * nb + (nb > 0 ? kSegW : 0);
         }
         if (lane == 63) s_pref[BV] = incl;
 #pragma unroll
@@ -178,13 +184,14 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     auto ntiles = [&](int v) { return (seq_of(v) + T - 1) / T; };
     auto mid_of = [&](int v, int t) -> int64_t {
         const int nb = (seq_of(v) + kStepTok - 1) / kStepTok;
-        return lds_uniform(&s_pref[v]) + 2LL * NBLK * t + min(NBLK, nb - t * NBLK);
+        // tile 0 spans kSegW + 2 nvs steps, tile t > 0 spans 2 nvs steps after kSegW + 2 NBLK t
+        return lds_uniform(&s_pref[v]) + (t == 0 ? kSegW / 2 : kSegW) + 2LL * NBLK * t + min(NBLK, nb - t * NBLK);
     };
     auto owner = [&](int64_t x) -> int { return (int)(((x + 1) * Geff - 1) / C); };
     // first tile t of non-empty v with mid(v, t) >= x (ntiles(v) if none)
     auto first_tile_from = [&](int v, int64_t x) -> int {
         const int nt = ntiles(v);
-        const int64_t d = x - lds_uniform(&s_pref[v]) - NBLK;          // mid of a full tile t: pv + NBLK (2t + 1)
+        const int64_t d = x - lds_uniform(&s_pref[v]) - kSegW - NBLK;  // mid of a full tile t > 0: pv + kSegW + NBLK (2t + 1)
         int t = d <= 0 ? 0 : (int)min((int64_t)nt, (d + 2 * NBLK - 1) / (2 * NBLK));
         while (t > 0 && mid_of(v, t - 1) >= x) --t;                  // the last tile's midpoint is earlier
         while (t < nt && mid_of(v, t) < x) ++t;
@@ -198,6 +205,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     struct Unit {
         int v, b, h0, t, seq, nvs;        // nvs = valid blocks (steps per pass); 0 = no unit
         int ids;                          // lane i < NBLK: physical block of block i of the tile
+        int raw[NBLK];                    // the table entries as loaded (scalar), until finish_ids
     };
     auto make_unit = [&](int v, int t, bool ok) -> Unit {
         Unit u;
@@ -207,16 +215,21 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         u.t = t;
         u.seq = ok ? seq_of(v) : 0;
         u.nvs = ok ? min(NBLK, (u.seq + kStepTok - 1) / kStepTok - t * NBLK) : 0;
-        // block ids live in one VGPR (lane i = block i) to keep scalar registers free
-        int raw[NBLK];
+        // the scalar table loads are only issued here; finish_ids, called when the unit's
+        // first step is about to be issued, waits for them (they then have long arrived)
 #pragma unroll
         for (int i = 0; i < NBLK; ++i)
-            raw[i] = ok ? ld_uniform(a.block_table, (int64_t)u.b * a.max_blocks + min(t * NBLK + i, a.max_blocks - 1)) : 0;
+            u.raw[i] = ok ? ld_uniform(a.block_table, (int64_t)u.b * a.max_blocks + min(t * NBLK + i, a.max_blocks - 1)) : 0;
         u.ids = 0;
+        return u;
+    };
+    // block ids into one VGPR (lane i = block i) to keep scalar registers free
+    auto finish_ids = [&](Unit& u) {
+        int ids = 0;
 #pragma unroll
         for (int i = 0; i < NBLK; ++i)
-            u.ids = (lane == i) ? ((i < u.nvs && raw[i] >= 0 && raw[i] < a.num_blocks) ? raw[i] : 0) : u.ids;
-        return u;
+            ids = (lane == i) ? ((i < u.nvs && u.raw[i] >= 0 && u.raw[i] < a.num_blocks) ? u.raw[i] : 0) : ids;
+        u.ids = ids;
     };
     // the unit after (v, t) in this workgroup's range, or none
     auto next_unit = [&](const Unit& u) -> Unit {
@@ -247,8 +260,10 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         }
         if (v >= BV || mid_of(v, t) >= hi) return;   // no midpoint in this range: no work
         cur = make_unit(v, t, true);
+        finish_ids(cur);
     }
     Unit nxt = next_unit(cur);
+    bool nxt_ready = false;                  // finish_ids(nxt) done
 
     // ---- per-lane constants of the staged layout ----------------------------------------------
     // Slot (token t, physical piece pp) holds logical piece pp ^ (t mod NPC) of token t.
@@ -354,6 +369,10 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             issue(cur, nidx, st);
         } else {
             const int k = nidx - 2 * cur.nvs;   // 0 or 1; the next unit has >= 2 steps
+            if (!nxt_ready) {
+                finish_ids(nxt);
+                nxt_ready = true;
+            }
             if (k == 0 && nxt.nvs > 0 && nxt.v != cur.v) {
                 issue_q(nxt.b, nxt.h0, nseg_issued & 1);
                 ++nseg_issued;
@@ -671,6 +690,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         if (nxt.nvs == 0) break;
         cur = nxt;
         nxt = next_unit(cur);
+        nxt_ready = false;
     }
     // drain the ring before the workgroup retires (loads past the last unit may be in flight)
     wait_vm<0>();
@@ -702,7 +722,9 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
     constexpr int T = NBLK * kStepTok;
     const int nt = (seq + T - 1) / T, nb = (seq + kStepTok - 1) / kStepTok;
     if (nt == 0) return;
-    auto mid_of = [&](int t) -> int64_t { return pv + 2LL * NBLK * t + min(NBLK, nb - t * NBLK); };
+    auto mid_of = [&](int t) -> int64_t {
+        return pv + (t == 0 ? kSegW / 2 : kSegW) + 2LL * NBLK * t + min(NBLK, nb - t * NBLK);
+    };
     auto owner = [&](int64_t x) -> int { return (int)(((x + 1) * Geff - 1) / C); };
     const int g0 = owner(mid_of(0)), g1 = owner(mid_of(nt - 1));
     if (g0 == g1) return;                      // finished in place by the decode kernel
@@ -714,7 +736,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
         } else if (i < n) {
             // first tile whose midpoint is >= the start of workgroup g0 + i's range
             const int64_t x = (int64_t)(g0 + i) * C / Geff;
-            const int64_t d = x - pv - NBLK;
+            const int64_t d = x - pv - kSegW - NBLK;
             int t = d <= 0 ? 0 : (int)min((int64_t)nt, (d + 2 * NBLK - 1) / (2 * NBLK));
             while (t > 0 && mid_of(t - 1) >= x) --t;
             while (t < nt && mid_of(t) < x) ++t;
