@@ -149,6 +149,7 @@ void decode_kernel(DecodeParams a) {
             const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
             const float qs = a.q_scale[qrow];
             qcoef[rb] = qs * a.softmax_scale * kLog2e;
+            const QRecip qd = q_recip(qs);
             const uint16_t* qp = a.q + qrow * kHeadDim;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -157,7 +158,7 @@ void decode_kernel(DecodeParams a) {
                 const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + d0 + 8);
                 const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
                                          (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
-                quantise_q16(raw, qs, &wds[half * 4]);
+                quantise_q16(raw, qd, &wds[half * 4]);
             }
             if (DBG && sp == 0 && w == 0 && a.dbg_q8) {
                 uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;

@@ -177,9 +177,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 
     // Unit (v, t) spans cost [s_pref[v] + 2 NBLK t, + 2 nvs); its midpoint mid(v, t)
     // decides its workgroup: workgroup g owns the units whose midpoints lie in [lo, hi),
-    // so a range is off its share by at most half a unit.  owner(x) is the workgroup
-    // whose range holds x.
-    const int64_t lo = (int64_t)g * C / Geff, hi = (int64_t)(g + 1) * C / Geff;
+    // so a range is off its share by at most half a unit.
+    const int lo = (int)((int64_t)g * C / Geff), hi = (int)((int64_t)(g + 1) * C / Geff);
     auto seq_of = [&](int v) { return lds_uniform(&s_seq[v / NG]); };
     auto ntiles = [&](int v) { return (seq_of(v) + T - 1) / T; };
     auto mid_of = [&](int v, int t) -> int64_t {
@@ -187,7 +186,6 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         // tile 0 spans kSegW + 2 nvs steps, tile t > 0 spans 2 nvs steps after kSegW + 2 NBLK t
         return lds_uniform(&s_pref[v]) + (t == 0 ? kSegW / 2 : kSegW) + 2LL * NBLK * t + min(NBLK, nb - t * NBLK);
     };
-    auto owner = [&](int64_t x) -> int { return (int)(((x + 1) * Geff - 1) / C); };
     // first tile t of non-empty v with mid(v, t) >= x (ntiles(v) if none)
     auto first_tile_from = [&](int v, int64_t x) -> int {
         const int nt = ntiles(v);
@@ -202,19 +200,27 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         return v;
     };
 
+    // A unit carries its sequence's batch, head group and length, so that stepping to the
+    // next tile of the same sequence divides nothing.
     struct Unit {
-        int v, b, h0, t, seq, nvs;        // nvs = valid blocks (steps per pass); 0 = no unit
-        int ids;                          // lane i < NBLK: physical block of block i of the tile
-        int raw[NBLK];                    // the table entries as loaded (scalar), until finish_ids
+        int v, b, h0, t, seq;
+        int nvs;                             // valid blocks (steps per pass); 0 = no unit
+        int ids;                             // lane i < NBLK: physical block of block i of the tile
+        int raw[NBLK];                       // the table entries as loaded (scalar), until finish_ids
     };
-    auto make_unit = [&](int v, int t, bool ok) -> Unit {
+    auto nblocks = [&](int seq) { return (seq + kStepTok - 1) / kStepTok; };
+    auto unit_mid = [&](const Unit& u, int t) -> int {
+        return lds_uniform(&s_pref[u.v]) + (t == 0 ? kSegW / 2 : kSegW) + 2 * NBLK * t + min(NBLK, nblocks(u.seq) - t * NBLK);
+    };
+    // (v, b, h0, seq) name a sequence; t its tile; !ok = no unit
+    auto make_unit = [&](int v, int b, int h0, int seq, int t, bool ok) -> Unit {
         Unit u;
         u.v = v;
-        u.b = ok ? v / NG : 0;
-        u.h0 = ok ? (v - u.b * NG) * HG : 0;
+        u.b = ok ? b : 0;
+        u.h0 = ok ? h0 : 0;
         u.t = t;
-        u.seq = ok ? seq_of(v) : 0;
-        u.nvs = ok ? min(NBLK, (u.seq + kStepTok - 1) / kStepTok - t * NBLK) : 0;
+        u.seq = ok ? seq : 0;
+        u.nvs = ok ? min(NBLK, nblocks(u.seq) - t * NBLK) : 0;
         // the scalar table loads are only issued here; finish_ids, called when the unit's
         // first step is about to be issued, waits for them (they then have long arrived)
 #pragma unroll
@@ -231,15 +237,27 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             ids = (lane == i) ? ((i < u.nvs && u.raw[i] >= 0 && u.raw[i] < a.num_blocks) ? u.raw[i] : 0) : ids;
         u.ids = ids;
     };
-    // the unit after (v, t) in this workgroup's range, or none
+    // the unit after u in this workgroup's range, or none
     auto next_unit = [&](const Unit& u) -> Unit {
-        int v = u.v, t = u.t + 1;
-        if (t >= ntiles(v)) {
-            v = next_nonempty(v + 1);
-            t = 0;
+        if (u.t + 1 < (u.seq + T - 1) / T) {
+            const bool ok = unit_mid(u, u.t + 1) < hi;
+            return make_unit(u.v, u.b, u.h0, u.seq, u.t + 1, ok);
         }
-        const bool ok = v < BV && mid_of(v, t) < hi;
-        return make_unit(ok ? v : 0, t, ok);
+        // the next non-empty sequence: later groups of this batch, then later batches
+        int v = u.v + 1, b = u.b, h0 = u.h0 + HG;
+        if (h0 == nkv) {
+            h0 = 0;
+            ++b;
+        }
+        int seq = 0;
+        while (v < BV && (seq = lds_uniform(&s_seq[b])) == 0) {
+            v += (nkv - h0) / HG;
+            ++b;
+            h0 = 0;
+        }
+        if (v >= BV) return make_unit(0, 0, 0, 0, 0, false);
+        const bool ok = lds_uniform(&s_pref[v]) + kSegW / 2 + min(NBLK, nblocks(seq)) < hi;   // tile 0's midpoint
+        return make_unit(v, b, h0, seq, 0, ok);
     };
 
     // first unit: the first midpoint >= lo
@@ -259,7 +277,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             }
         }
         if (v >= BV || mid_of(v, t) >= hi) return;   // no midpoint in this range: no work
-        cur = make_unit(v, t, true);
+        const int b = v / NG;
+        cur = make_unit(v, b, (v - b * NG) * HG, seq_of(v), t, true);
         finish_ids(cur);
     }
     Unit nxt = next_unit(cur);
@@ -419,6 +438,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                             const int sr = hl * rows + rr;
                             const float qs = s_qs[vs_buf][sr];
                             qcoef[rb] = qs * a.softmax_scale * kLog2e;
+                            const QRecip qd = q_recip(qs);
 #pragma unroll
                             for (int hlf = 0; hlf < 2; ++hlf) {
                                 const uint8_t* qp = s_q[vs_buf] + sr * 256 + (hlf * 64 + 16 * lg) * 2;
@@ -426,7 +446,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                                 const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + 16);
                                 const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
                                                          (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
-                                quantise_q16(raw, qs, &wds[hlf * 4]);
+                                quantise_q16(raw, qd, &wds[hlf * 4]);
                             }
                             if (DBG && a.dbg_q8 && p == 0) {
                                 const int s = rr / a.G, gq = rr - s * a.G;
@@ -614,8 +634,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         // ---- end of a (batch, group) segment in this workgroup --------------------------------
         const bool seg_end = nxt.nvs == 0 || nxt.v != cur.v;
         if (seg_end) {
-            const int nt = ntiles(cur.v);
-            const bool split = owner(mid_of(cur.v, 0)) != owner(mid_of(cur.v, nt - 1));
+            // finished here unless some tile of the sequence lies outside this range
+            const bool split = unit_mid(cur, 0) < lo || unit_mid(cur, (cur.seq + T - 1) / T - 1) >= hi;
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 // the two halves of each head: wave p = 1 hands its O and L to wave p = 0

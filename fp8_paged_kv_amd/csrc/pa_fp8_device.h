@@ -105,21 +105,48 @@ __device__ __forceinline__ int chunk_token(int g, int j) {
 }
 
 // Step 1 of the decode for 16 bf16 query values of one row: code = E4M3(q / qs),
-// the division in IEEE FP32 (the codes are decided in FP32), saturated to
-// +-448 (the gfx950 convert rounds to nearest even but does not clamp).
-// raw: 8 dwords = 16 bf16; out: 4 dwords of codes, byte i = value i.
-__device__ __forceinline__ void quantise_q16(const uint32_t raw[8], float qs, uint32_t out[4]) {
+// the quotient rounded as an IEEE FP32 division (the codes are decided in FP32),
+// saturated to +-448 (the gfx950 convert rounds to nearest even but does not
+// clamp).  raw: 8 dwords = 16 bf16; out: 4 dwords of codes, byte i = value i.
+//
+// One division per row instead of one per value: with y = RN(1/qs) and the
+// product q0 = RN(q y) (a faithful quotient), the residual q - qs q0 is exact
+// in one FMA and q0 + residual * y rounds to RN(q / qs) (Markstein's
+// correction, IBM J. Res. Dev. 34(1), 1990).  It needs the residual to stay
+// normal: taken for qs in [2^-60, 2^60] and quotients below 2048 in magnitude
+// (a larger one saturates to 448 from either value; a zero keeps its sign);
+// any other qs (0, negative, tiny, huge, NaN) divides value by value.
+struct QRecip {
+    float qs, y;
+    bool fast;
+};
+__device__ __forceinline__ QRecip q_recip(float qs) {
+    QRecip r;
+    r.qs = qs;
+    r.fast = qs >= 0x1p-60f && qs <= 0x1p60f;
+    r.y = r.fast ? 1.f / qs : 0.f;
+    return r;
+}
+__device__ __forceinline__ void quantise_q16(const uint32_t raw[8], const QRecip& d, uint32_t out[4]) {
     float x[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         x[2 * i] = bf16_to_f32((uint16_t)(raw[i] & 0xffffu));
         x[2 * i + 1] = bf16_to_f32((uint16_t)(raw[i] >> 16));
     }
+    if (d.fast) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float y = (qs == 0.f) ? 0.f : x[i] / qs;
-        x[i] = __builtin_amdgcn_fmed3f(y, -448.f, 448.f);
+        for (int i = 0; i < 16; ++i) {
+            float q = x[i] * d.y;
+            if (q != 0.f && fabsf(q) < 2048.f) q = __builtin_fmaf(__builtin_fmaf(-d.qs, q, x[i]), d.y, q);
+            x[i] = q;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (d.qs == 0.f) ? 0.f : x[i] / d.qs;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_fmed3f(x[i], -448.f, 448.f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = cvt4_fp8(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
 }

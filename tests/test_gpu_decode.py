@@ -61,6 +61,41 @@ def test_config0_gather_and_q_codes_bit_exact(B, oracle_mod):
     compare(gpu_out_float(out), ref["out_bf16"], "config0 debug")
 
 
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_q_codes_wide_scales_bit_exact(B, oracle_mod, num_splits):
+    """Step 1's FP8 query codes on both paths (0: whole-row, 1: per-head) for
+    q_scale drawn over 2^-70 .. 2^70 (across the range where the kernels divide
+    through one reciprocal per row and the range where they divide per value),
+    powers of two, zeros and negative scales, and query values of every
+    binade: the codes equal the oracle's FP32 division, byte for byte."""
+    cfg = _case("qcodes", B=3, s1=2, nq=16, nkv=2, seq_lens=(5, 130, 300), num_blocks=10, max_blocks_per_seq=4,
+                seed=21)
+    inp = synth.make_gqa_inputs(cfg)
+    g = torch.Generator().manual_seed(22)
+    n = inp["q_scale"].numel()
+    mant = 1.0 + torch.rand(n, generator=g, dtype=torch.float64)
+    expo = torch.randint(-70, 71, (n,), generator=g).double()
+    qs = (mant * torch.pow(2.0, expo)).float()
+    qs[::7] = torch.pow(2.0, expo[::7]).float()                     # powers of two
+    qs[3::11] = 0.0
+    qs[5::13] = -qs[5::13]
+    inp["q_scale"] = qs.reshape(inp["q_scale"].shape).contiguous()
+    bits = torch.randint(0, 1 << 16, inp["q"].shape, generator=g, dtype=torch.int32)
+    bits = torch.where((bits & 0x7F80) == 0x7F80, bits & ~0x4000, bits)     # no inf / NaN queries
+    inp["q"] = bits.to(torch.int16).view(torch.bfloat16).contiguous()
+    ref = oracle_mod.gqa_decode(inp)
+    print(f"[gpu] q codes, wide scales, splits={num_splits}", flush=True)
+    d = to_device(inp)
+    _, _, q8 = B.decode_debug(d["q"], d["q_scale"], d["k_cache"], d["k_scale"], d["v_cache"], d["v_scale"],
+                              d["block_table"], d["kv_act_seqs"], d["softmax_scale"], cfg.s2_tile,
+                              num_splits=num_splits)
+    torch.cuda.synchronize()
+    got = q8.cpu().numpy()
+    if not np.array_equal(got, ref["q8"]):
+        bad = np.argwhere(got != ref["q8"])
+        raise AssertionError(f"{len(bad)} codes differ, first {bad[:4].tolist()}")
+
+
 @pytest.mark.parametrize("s2_tile", [128, 256, 512, 1024, 2048])
 def test_tile_sizes(B, oracle_mod, s2_tile):
     cfg = _case(f"tile{s2_tile}", seq_lens=(1, 127, 129, 1500, 2048, 2100), B=6, nq=8, nkv=2,
