@@ -166,12 +166,12 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         // the partition, for the merge kernel: cost prefix over (batch, group), then Geff
         for (int i = threadIdx.x; i <= BV; i += NW * 64) a.rows_meta[i] = s_pref[i];
         if (threadIdx.x == 0) a.rows_meta[BV + 1] = Geff;
-        // rows of empty sequences are zero
-        for (int b = 0; b < B; ++b) {
-            if (s_seq[b] != 0) continue;
-            for (int e = threadIdx.x; e < a.s1 * a.nq * kHeadDim; e += NW * 64)
-                a.out[(int64_t)b * a.s1 * a.nq * kHeadDim + e] = 0;
-        }
+    }
+    // rows of empty sequences are zero: workgroup g clears batches g, g + grid, ...
+    for (int b = g; b < B; b += gridDim.x) {
+        if (lds_uniform(&s_seq[b]) != 0) continue;
+        for (int e = threadIdx.x; e < a.s1 * a.nq * kHeadDim; e += NW * 64)
+            a.out[(int64_t)b * a.s1 * a.nq * kHeadDim + e] = 0;
     }
     if (g >= Geff) return;
 
@@ -179,27 +179,6 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     // decides its workgroup: workgroup g owns the units whose midpoints lie in [lo, hi),
     // so a range is off its share by at most half a unit.
     const int lo = (int)((int64_t)g * C / Geff), hi = (int)((int64_t)(g + 1) * C / Geff);
-    auto seq_of = [&](int v) { return lds_uniform(&s_seq[v / NG]); };
-    auto ntiles = [&](int v) { return (seq_of(v) + T - 1) / T; };
-    auto mid_of = [&](int v, int t) -> int64_t {
-        const int nb = (seq_of(v) + kStepTok - 1) / kStepTok;
-        // tile 0 spans kSegW + 2 nvs steps, tile t > 0 spans 2 nvs steps after kSegW + 2 NBLK t
-        return lds_uniform(&s_pref[v]) + (t == 0 ? kSegW / 2 : kSegW) + 2LL * NBLK * t + min(NBLK, nb - t * NBLK);
-    };
-    // first tile t of non-empty v with mid(v, t) >= x (ntiles(v) if none)
-    auto first_tile_from = [&](int v, int64_t x) -> int {
-        const int nt = ntiles(v);
-        const int64_t d = x - lds_uniform(&s_pref[v]) - kSegW - NBLK;  // mid of a full tile t > 0: pv + kSegW + NBLK (2t + 1)
-        int t = d <= 0 ? 0 : (int)min((int64_t)nt, (d + 2 * NBLK - 1) / (2 * NBLK));
-        while (t > 0 && mid_of(v, t - 1) >= x) --t;                  // the last tile's midpoint is earlier
-        while (t < nt && mid_of(v, t) < x) ++t;
-        return t;
-    };
-    auto next_nonempty = [&](int v) {
-        while (v < BV && ntiles(v) == 0) ++v;
-        return v;
-    };
-
     // A unit carries its sequence's batch, head group and length, so that stepping to the
     // next tile of the same sequence divides nothing.
     struct Unit {
@@ -260,28 +239,49 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         return make_unit(v, b, h0, seq, 0, ok);
     };
 
-    // first unit: the first midpoint >= lo
+    // first unit: the first midpoint >= lo.  The largest v with s_pref[v] <= lo is found
+    // with two rounds of 64 parallel LDS reads; it is a non-empty sequence (an empty one
+    // would share its prefix with v + 1, and s_pref[BV] = C > lo).
     Unit cur;
     {
-        int vlo = 0, vhi = BV - 1;            // largest v with s_pref[v] <= lo
-        while (vlo < vhi) {
-            const int mid = (vlo + vhi + 1) >> 1;
-            if (lds_uniform(&s_pref[mid]) <= lo) vlo = mid; else vhi = mid - 1;
-        }
-        int v = next_nonempty(vlo), t = 0;
-        if (v < BV) {
-            t = first_tile_from(v, lo);
-            if (t >= ntiles(v)) {
-                v = next_nonempty(v + 1);
-                t = 0;
+        const int stride = (BV + 63) / 64;
+        const uint64_t m1 = __ballot(s_pref[min(lane * stride, BV - 1)] <= lo);
+        const int base = min((__popcll(m1) - 1) * stride, BV - 1);
+        const uint64_t m2 = __ballot(lane < stride && s_pref[min(base + lane, BV - 1)] <= lo);
+        int v = __builtin_amdgcn_readfirstlane(min(base + __popcll(m2) - 1, BV - 1));
+        int b = v / NG, h0 = (v - b * NG) * HG;
+        int seq = lds_uniform(&s_seq[b]);
+        int pv = lds_uniform(&s_pref[v]);
+        const int nbv = nblocks(seq), ntv = (seq + T - 1) / T;
+        auto midv = [&](int t) { return pv + (t == 0 ? kSegW / 2 : kSegW) + 2 * NBLK * t + min(NBLK, nbv - t * NBLK); };
+        const int d = lo - pv - kSegW - NBLK;       // mid of a full tile t > 0: pv + kSegW + NBLK (2t + 1)
+        int t = d <= 0 ? 0 : min(ntv, (d + 2 * NBLK - 1) / (2 * NBLK));
+        while (t > 0 && midv(t - 1) >= lo) --t;    // the last tile's midpoint is earlier
+        while (t < ntv && midv(t) < lo) ++t;
+        int mid;
+        if (t < ntv) {
+            mid = midv(t);
+        } else {
+            // every midpoint of v lies below lo: tile 0 of the next non-empty sequence
+            t = 0;
+            seq = 0;
+            while (seq == 0) {
+                ++v;
+                h0 += HG;
+                if (h0 == nkv) {
+                    h0 = 0;
+                    ++b;
+                }
+                if (v >= BV) return;
+                seq = lds_uniform(&s_seq[b]);
             }
+            pv = lds_uniform(&s_pref[v]);
+            mid = pv + kSegW / 2 + min(NBLK, nblocks(seq));
         }
-        if (v >= BV || mid_of(v, t) >= hi) return;   // no midpoint in this range: no work
-        const int b = v / NG;
-        cur = make_unit(v, b, (v - b * NG) * HG, seq_of(v), t, true);
-        finish_ids(cur);
+        if (mid >= hi) return;                      // no midpoint in this range: no work
+        cur = make_unit(v, b, h0, seq, t, true);   // its table loads overlap the Q staging below
     }
-    Unit nxt = next_unit(cur);
+    Unit nxt;
     bool nxt_ready = false;                  // finish_ids(nxt) done
 
     // ---- per-lane constants of the staged layout ----------------------------------------------
@@ -326,27 +326,37 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     };
 
     // The QNW loads of this wave that stage the query rows and q_scale of heads
-    // h0 .. h0+HG-1 of batch b (staged row hl * rows + rr) and their v_scale.
-    // Rare (once per sequence), so the lane values are recomputed on every call.
+    // h0 .. h0+HG-1 of batch b (staged row hl * rows + rr) and their v_scale.  Staged
+    // row sr = hs * rows + s * G + gq is query row b s1 nq + s nq + (h0 + hs) G + gq; the
+    // part that depends on neither b nor h0 is a per-lane constant (-1: padding row).
     const int rows = a.rows;
-    auto issue_q = [&](int b, int h0, int buf) {
+    int qoff[QNW];
+    {
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int qrow0 = b * a.s1 * a.nq;                     // first query row of batch b
-        auto src_row = [&](int sr) {                            // staged row -> query row
+        auto off_of = [&](int sr) {
             const int hs = sr / rows, rr = sr - hs * rows;
             const int s = rr / a.G, gq = rr - s * a.G;
-            return qrow0 + s * a.nq + (h0 + hs) * a.G + gq;
+            return sr < HG * rows ? s * a.nq + hs * a.G + gq : -1;
         };
 #pragma unroll
         for (int n = 0; n < QNW; ++n) {
             const int j = w + n * NW;
+            qoff[n] = j < QI ? off_of(4 * j + (ln >> 4)) : (j == QI ? off_of(ln) : -1);
+        }
+    }
+    auto issue_q = [&](int b, int h0, int buf) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int qrow0 = b * a.s1 * a.nq;                     // first query row of batch b
+        const int qrowh = qrow0 + h0 * a.G;
+#pragma unroll
+        for (int n = 0; n < QNW; ++n) {
+            const int j = w + n * NW;
+            const int row = qoff[n] >= 0 ? qrowh + qoff[n] : qrow0;
             if (j < QI) {
-                const int sr = 4 * j + (ln >> 4);
-                const int row = sr < HG * rows ? src_row(sr) : qrow0;
                 dma16(a.q, (uint32_t)(row * 256 + 16 * (ln & 15)), (lds_ptr)(&s_q[buf][j * 1024]));
             } else if (j == QI) {
-                const int row = ln < HG * rows ? src_row(ln) : qrow0;
                 dma4(a.q_scale, (uint32_t)(row * 4), (lds_ptr)(&s_qs[buf][0]));
             } else if (j == QI + 1) {
                 const uint32_t vb = (uint32_t)((b * nkv + h0) * kHeadDim * 4);
@@ -371,8 +381,10 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     int last_q_step = 0;                     // step whose loads followed the latest Q staging
     int nseg_issued = 1;                     // sequences staged so far (segment i uses buffer i & 1)
     int vs_buf = 1;
+    finish_ids(cur);
     issue(cur, 0, 0);
     issue(cur, 1, 1);
+    nxt = next_unit(cur);
     int gs = 0;                              // global step index (ring position)
     int prev_v = -1;
 
