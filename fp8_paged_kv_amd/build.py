@@ -23,8 +23,11 @@ def hipcc() -> str:
 
 # Per-source extra flags.  The whole-row kernels unroll a whole tile so that its
 # scores stay in statically indexed registers; LLVM's default size cap for
-# "#pragma unroll" would stop that.
-EXTRA = {"pa_fp8_decode_rows.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+# "#pragma unroll" would stop that.  Their MFMA accumulators are kept in
+# architectural VGPRs: left to its heuristics the compiler keeps O in VGPRs
+# between steps and copies it to AGPRs and back around every P.V step
+# (64 extra moves per step).
+EXTRA = {"pa_fp8_decode_rows.hip": ["-mllvm", "-pragma-unroll-threshold=1000000", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> str:
