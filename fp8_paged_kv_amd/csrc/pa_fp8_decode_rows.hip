@@ -78,6 +78,14 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
 
 __device__ __forceinline__ int lds_uniform(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
 
+// floor(x / d) for 0 <= x and x + d < 2^22, given inv = 1.0f / d (IEEE): (x + 0.5) / d lies at
+// least 0.5 / d from an integer and the two roundings move it by less than that.
+__device__ __forceinline__ int small_div(int x, float inv) { return (int)(((float)x + 0.5f) * inv); }
+
+// floor(num / den) for 0 <= num < 2^53, den > 0 and a quotient below 2^31, in double precision:
+// a non-integer quotient is at least 1 / den from the next integer, far beyond the rounding.
+__device__ __forceinline__ int floor_div64(int64_t num, int64_t den) { return (int)((double)num / (double)den); }
+
 constexpr int kStepTok = 128;             // tokens per step = one cache block
 constexpr int kPrefixMax = 1024;          // (batch, head group) pairs of one call
 // Cost of starting a (batch, group) sequence in a workgroup (staging and converting its
@@ -122,6 +130,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     const int lr = lane & 15, lg = lane >> 4;
     const int B = a.B, NG = a.nkv / HG, BV = B * NG;
     const int nkv = a.nkv;
+    const float inv_ng = 1.0f / NG, inv_g = 1.0f / a.G;
 
     // ---- lengths, cost prefix and unit count ------------------------------------------------
     for (int b = threadIdx.x; b < B; b += NW * 64) {
@@ -132,12 +141,17 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     if (w == 0) {
         const int strip = (BV + 63) / 64;
         const int v0 = lane * strip, v1 = min(v0 + strip, BV);
+        const int bs0 = small_div(v0, inv_ng), gs0 = v0 - bs0 * NG;   // batch and group of v0
         int cost = 0, units = 0;
-        for (int v = v0; v < v1; ++v) {
-            const int s = s_seq[v / NG];
+        for (int v = v0, bb = bs0, gg = gs0; v < v1; ++v) {
+            const int s = s_seq[bb];
             const int nb = (s + kStepTok - 1) / kStepTok;
             cost += 2 * nb + (nb > 0 ? kSegW : 0);
             units += (s + T - 1) / T;
+            if (++gg == NG) {
+                gg = 0;
+                ++bb;
+            }
         }
         int incl = cost;
 #pragma unroll
@@ -146,10 +160,14 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             if (lane >= o) incl += x;
         }
         int run = incl - cost;
-        for (int v = v0; v < v1; ++v) {
+        for (int v = v0, bb = bs0, gg = gs0; v < v1; ++v) {
             s_pref[v] = run;
-            const int nb = (s_seq[v / NG] + kStepTok - 1) / kStepTok;
+            const int nb = (s_seq[bb] + kStepTok - 1) / kStepTok;
             run += 2 * nb + (nb > 0 ? kSegW : 0);
+            if (++gg == NG) {
+                gg = 0;
+                ++bb;
+            }
         }
         if (lane == 63) s_pref[BV] = incl;
 #pragma unroll
@@ -178,7 +196,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     // Unit (v, t) spans cost [s_pref[v] + 2 NBLK t, + 2 nvs); its midpoint mid(v, t)
     // decides its workgroup: workgroup g owns the units whose midpoints lie in [lo, hi),
     // so a range is off its share by at most half a unit.
-    const int lo = (int)((int64_t)g * C / Geff), hi = (int)((int64_t)(g + 1) * C / Geff);
+    const int lo = floor_div64((int64_t)g * C, Geff), hi = floor_div64((int64_t)(g + 1) * C, Geff);
     // A unit carries its sequence's batch, head group and length, so that stepping to the
     // next tile of the same sequence divides nothing.
     struct Unit {
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         const int base = min((__popcll(m1) - 1) * stride, BV - 1);
         const uint64_t m2 = __ballot(lane < stride && s_pref[min(base + lane, BV - 1)] <= lo);
         int v = __builtin_amdgcn_readfirstlane(min(base + __popcll(m2) - 1, BV - 1));
-        int b = v / NG, h0 = (v - b * NG) * HG;
+        int b = small_div(v, inv_ng), h0 = (v - b * NG) * HG;
         int seq = lds_uniform(&s_seq[b]);
         int pv = lds_uniform(&s_pref[v]);
         const int nbv = nblocks(seq), ntv = (seq + T - 1) / T;
@@ -334,9 +352,10 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     {
         int ln = lane;
         asm volatile("" : "+v"(ln));
+        const float inv_rows = 1.0f / rows;
         auto off_of = [&](int sr) {
-            const int hs = sr / rows, rr = sr - hs * rows;
-            const int s = rr / a.G, gq = rr - s * a.G;
+            const int hs = small_div(sr, inv_rows), rr = sr - hs * rows;
+            const int s = small_div(rr, inv_g), gq = rr - s * a.G;
             return sr < HG * rows ? s * a.nq + hs * a.G + gq : -1;
         };
 #pragma unroll
@@ -444,7 +463,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                         uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                         qcoef[rb] = 0.f;
                         // causal decode: position s of s1 attends to the first seq - s1 + 1 + s tokens
-                        lim[rb] = cur.seq - (a.causal ? a.s1 - 1 - (rr < rows ? rr / a.G : a.s1 - 1) : 0);
+                        lim[rb] = cur.seq - (a.causal ? a.s1 - 1 - (rr < rows ? small_div(rr, inv_g) : a.s1 - 1) : 0);
                         mlim = cur.seq - (a.causal ? a.s1 - 1 : 0);
                         if (rr < rows) {
                             const int sr = hl * rows + rr;
@@ -461,7 +480,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                                 quantise_q16(raw, qd, &wds[hlf * 4]);
                             }
                             if (DBG && a.dbg_q8 && p == 0) {
-                                const int s = rr / a.G, gq = rr - s * a.G;
+                                const int s = small_div(rr, inv_g), gq = rr - s * a.G;
                                 const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
                                 uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;
 #pragma unroll
@@ -683,7 +702,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                         const int rr = rb * 16 + 4 * lg + i;
                         const float Lr = __shfl(Lw, 4 * lg + i, 64);
                         if (rr >= rows) continue;
-                        const int s = rr / a.G, gq = rr - s * a.G;
+                        const int s = small_div(rr, inv_g), gq = rr - s * a.G;
                         const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
                         if (!split) {
                             // step 10: out = O * v_scale / L' (L' = 448 L), bf16
@@ -757,7 +776,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
     auto mid_of = [&](int t) -> int64_t {
         return pv + (t == 0 ? kSegW / 2 : kSegW) + 2LL * NBLK * t + min(NBLK, nb - t * NBLK);
     };
-    auto owner = [&](int64_t x) -> int { return (int)(((x + 1) * Geff - 1) / C); };
+    auto owner = [&](int64_t x) -> int { return floor_div64((x + 1) * Geff - 1, C); };
     const int g0 = owner(mid_of(0)), g1 = owner(mid_of(nt - 1));
     if (g0 == g1) return;                      // finished in place by the decode kernel
     const int n = g1 - g0 + 1;                 // <= the decode grid (<= 256)
@@ -767,7 +786,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
             tf = 0;
         } else if (i < n) {
             // first tile whose midpoint is >= the start of workgroup g0 + i's range
-            const int64_t x = (int64_t)(g0 + i) * C / Geff;
+            const int64_t x = floor_div64((int64_t)(g0 + i) * C, Geff);
             const int64_t d = x - pv - kSegW - NBLK;
             int t = d <= 0 ? 0 : (int)min((int64_t)nt, (d + 2 * NBLK - 1) / (2 * NBLK));
             while (t > 0 && mid_of(t - 1) >= x) --t;
@@ -809,7 +828,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
             Mx = mn;
         }
     }
-    const int sq = rr / a.G, gq = rr - sq * a.G;
+    const int sq = small_div(rr, 1.0f / a.G), gq = rr - sq * a.G;
     const int64_t qrow = ((int64_t)b * a.s1 + sq) * a.nq + h * a.G + gq;
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint32_t pk[4];
