@@ -115,7 +115,9 @@ __device__ __forceinline__ int chunk_token(int g, int j) {
 // correction, IBM J. Res. Dev. 34(1), 1990).  It needs the residual to stay
 // normal: taken for qs in [2^-60, 2^60] and quotients below 2048 in magnitude
 // (a larger one saturates to 448 from either value; a zero keeps its sign);
-// any other qs (0, negative, tiny, huge, NaN) divides value by value.
+// for |q| < 2^-100 the residual may underflow and the quotient be one unit
+// off, but it is then below 2^-40 and its code is zero either way.  Any other
+// qs (0, negative, tiny, huge, NaN) divides value by value.
 struct QRecip {
     float qs, y;
     bool fast;
