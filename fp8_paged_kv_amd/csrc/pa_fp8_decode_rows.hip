@@ -713,7 +713,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                                 const int c0 = 2 * q2, c1 = 2 * q2 + 1;
                                 const float x0 = O[rb][c0][i] * (c0 < 4 ? vs0[c0] : vs1[c0 - 4]) * inv;
                                 const float x1 = O[rb][c1][i] * (c1 < 4 ? vs0[c1] : vs1[c1 - 4]) * inv;
-                                pk[q2] = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+                                pk[q2] = pack_bf16x2(x0, x1);
                             }
                             *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + 8 * lr) =
                                 i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
@@ -836,7 +836,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
     for (int c = 0; c < 4; ++c) {
         const float y0 = (c < 2 ? o0[2 * c] : o1[2 * c - 4]) * (c < 2 ? vs0[2 * c] : vs1[2 * c - 4]) * inv;
         const float y1 = (c < 2 ? o0[2 * c + 1] : o1[2 * c - 3]) * (c < 2 ? vs0[2 * c + 1] : vs1[2 * c - 3]) * inv;
-        pk[c] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+        pk[c] = pack_bf16x2(y0, y1);
     }
     *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + d0) = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
 }

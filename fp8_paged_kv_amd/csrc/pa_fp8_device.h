@@ -72,12 +72,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Two FP32 values -> two bf16 rounded to nearest even, low half = a: one
+// v_cvt_pk_bf16_f32.  For every one of the 2^32 inputs it gives the bits of
+// rounding the pattern by hand (add 0x7fff plus the kept lsb, keep the high
+// half; a NaN keeps its sign and top payload bits and becomes quiet), checked
+// on the device; subnormals are kept.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return (uint16_t)pack_bf16x2(x, 0.f); }
 
 // Broadcast lane n of every 16-lane row to the whole row (DPP row_newbcast).
 template <int N>

@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams a, int T) {
     for (int c = 0; c < 4; ++c) {
         const float y0 = (c < 2 ? o0[2 * c] : o1[2 * c - 4]) * inv;
         const float y1 = (c < 2 ? o0[2 * c + 1] : o1[2 * c - 3]) * inv;
-        pk[c] = (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+        pk[c] = pack_bf16x2(y0, y1);
     }
     *reinterpret_cast<i32x4*>(a.out + qh * kMlaNope + 8 * lane) = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
 }
