@@ -327,8 +327,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     const uint32_t ksoff = (uint32_t)(lane * nkv * 4);
 
     // Issue the loads of step `idx` of unit u (K pass: idx < nvs, then the V pass) into
-    // stage st: DPW block loads and one k_scale load per wave, always PER_STEP.  A step
-    // past the last unit (nvs == 0) reloads block 0.
+    // stage st: DPW block loads and one k_scale load per wave, always PER_STEP.  Nothing is
+    // issued past the last unit; the last step then waits for all loads.
     auto issue = [&](const Unit& u, int idx, int st) {
         const bool ok = u.nvs > 0;
         const bool isv = ok && idx >= u.nvs;
@@ -409,7 +409,9 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 
     // one step: wait for its loads, barrier, keep AHEAD steps in flight
     auto step_begin = [&](int idx) {
-        if (last_q_step == gs + 1)
+        if (idx + 1 >= 2 * cur.nvs && nxt.nvs == 0)
+            wait_vm<0>();                        // the last step: nothing was issued behind it
+        else if (last_q_step == gs + 1)
             wait_vm<PER_STEP * (AHEAD - 1) + QNW>();
         else
             wait_vm<PER_STEP * (AHEAD - 1)>();
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                 ++nseg_issued;
                 last_q_step = gs + AHEAD;
             }
-            issue(nxt, k, st);
+            if (nxt.nvs > 0) issue(nxt, k, st);
         }
     };
 
@@ -743,7 +745,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         nxt = next_unit(cur);
         nxt_ready = false;
     }
-    // drain the ring before the workgroup retires (loads past the last unit may be in flight)
+    // the workgroup retires with no load in flight (the last step waited for all of them)
     wait_vm<0>();
 }
 
