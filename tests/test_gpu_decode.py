@@ -96,6 +96,22 @@ def test_q_codes_wide_scales_bit_exact(B, oracle_mod, num_splits):
         raise AssertionError(f"{len(bad)} codes differ, first {bad[:4].tolist()}")
 
 
+@pytest.mark.parametrize("B_,nq,nkv", [(1024, 4, 1), (256, 32, 8)])
+def test_whole_row_most_pairs(B, oracle_mod, B_, nq, nkv):
+    """The largest (batch, head group) count the whole-row path takes (1024):
+    one head per workgroup (nkv odd) and two; mostly short sequences with a
+    long one every 64 batches, so ranges hold many whole sequences and some
+    sequences are split.  Every output row against the oracle."""
+    lens = [(37 * b) % 250 + 1 if b % 64 else 1500 + b for b in range(B_)]
+    mb = (max(lens) + 127) // 128
+    nblk = sum((x + 127) // 128 for x in lens) + 4
+    cfg = _case(f"pairs-{B_}x{nkv}", B=B_, nq=nq, nkv=nkv, seq_lens=tuple(lens), num_blocks=nblk,
+                max_blocks_per_seq=mb, s2_tile=256, seed=B_ + nkv)
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    compare(_run(B, inp, 0, "most pairs"), ref["out_bf16"], f"B={B_} nkv={nkv}")
+
+
 @pytest.mark.parametrize("s2_tile", [128, 256, 512, 1024, 2048])
 def test_tile_sizes(B, oracle_mod, s2_tile):
     cfg = _case(f"tile{s2_tile}", seq_lens=(1, 127, 129, 1500, 2048, 2100), B=6, nq=8, nkv=2,
