@@ -1,0 +1,94 @@
+"""The decode calls captured in a HIP graph (torch.cuda.CUDAGraph on ROCm):
+every replay, with eager calls and synchronisations between replays, gives
+the eager result bit for bit — the whole-row path (its per-call partition), the
+per-head path with splits (its arrival counters, left at zero by every call)
+and the MLA decode.  Workspaces and outputs are allocated before capture; the
+calls enqueue kernels only.  Every test prints its case first."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from fp8_paged_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp8_paged_kv_amd import binding
+    binding.lib()
+    return binding
+
+
+def _check_replays(run_eager, run_into, outs, tag):
+    """run_eager(stream) -> list of reference outputs; run_into(stream) enqueues the calls
+    writing `outs`.  Capture once, replay four times with eager work in between."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ref = [r.clone() for r in run_eager(s)]
+        run_into(s)                                   # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run_into(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, r), f"{tag}: replay {rep}, output {i} differs from the eager call"
+        with torch.cuda.stream(s):
+            run_eager(s)                              # eager calls between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_gqa_decode_graph_replays(B, num_splits):
+    cfg = synth.GqaConfig(name="graph", B=3, s1=1, nq=16, nkv=2, seq_lens=(300, 1100, 2500), s2_tile=256,
+                          num_blocks=40, max_blocks_per_seq=20, seed=31)
+    sets = [synth.make_gqa_inputs(cfg, device="cuda", seed=31 + i) for i in range(2)]
+    print(f"[gpu] graph replays, gqa decode, splits={num_splits}", flush=True)
+    need, _ = B.workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.nkv, cfg.D, cfg.block_size, cfg.max_blocks_per_seq,
+                               cfg.s2_tile, num_splits)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    shape = (cfg.B * cfg.s1, cfg.nq, cfg.D)
+    outs = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in sets]
+    eager_out = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in sets]
+
+    def run_eager(st):
+        for inp, o in zip(sets, eager_out):
+            B.decode_inputs(inp, num_splits=num_splits, out=o, workspace=ws, stream=st)
+        return eager_out
+
+    def run_into(st):
+        for inp, o in zip(sets, outs):
+            B.decode_inputs(inp, num_splits=num_splits, out=o, workspace=ws, stream=st)
+
+    _check_replays(run_eager, run_into, outs, f"gqa splits={num_splits}")
+
+
+def test_mla_decode_graph_replays(B):
+    cfg = synth.MlaConfig("graph-mla", B=2, s1=1, nq=32, topk=512, seq_range=(600, 1500), num_blocks=32,
+                          max_blocks_per_seq=16, s2_tile=256, seed=33)
+    inp = synth.make_mla_inputs(cfg, device="cuda")
+    print("[gpu] graph replays, mla decode", flush=True)
+    ws = torch.zeros(max(B.mla_workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.topk, cfg.s2_tile), 1),
+                     dtype=torch.uint8, device="cuda")
+    shape = (cfg.B * cfg.s1 * cfg.nq, 512)
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    eager_out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+
+    def run_eager(st):
+        B.mla_decode_inputs(inp, out=eager_out, workspace=ws, stream=st)
+        return [eager_out]
+
+    def run_into(st):
+        B.mla_decode_inputs(inp, out=out, workspace=ws, stream=st)
+
+    _check_replays(run_eager, run_into, [out], "mla")
