@@ -19,8 +19,9 @@
 //    vmcnt wait and a raw barrier at every step.
 //  * Work unit = one tile of one (batch, head group).  The units of the whole
 //    call, in (batch, group, tile) order, are split into contiguous ranges of
-//    equal cost (steps = 2 x valid blocks), one per workgroup; blocks past a
-//    sequence's end cost nothing and are not visited.  A (batch, group) whose
+//    equal cost (2 steps per valid block, plus a charge for each sequence
+//    start), one per workgroup; blocks past a sequence's end cost nothing and
+//    are not visited.  A (batch, group) whose
 //    tiles land in one workgroup is finished in place.  Otherwise every
 //    workgroup writes an (O, M, L) partial and a second, small kernel merges
 //    them (the kernel boundary orders the writes; no fences or atomics).
@@ -89,8 +90,9 @@ __device__ __forceinline__ int floor_div64(int64_t num, int64_t den) { return (i
 constexpr int kStepTok = 128;             // tokens per step = one cache block
 constexpr int kPrefixMax = 1024;          // (batch, head group) pairs of one call
 // Cost of starting a (batch, group) sequence in a workgroup (staging and converting its
-// query rows, and finishing its output), in steps: measured at about four steps.  The
-// partition charges it to the sequence's first tile.
+// query rows, and finishing its output), in steps; the partition charges it to the
+// sequence's first tile.  Measured at two to four steps; charges from 2 to 6 move the
+// slowest range by a tile's rounding either way.
 constexpr int kSegW = 4;
 
 template <int NRB, int NBLK, int HG, bool DBG>
