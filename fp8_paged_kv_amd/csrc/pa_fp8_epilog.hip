@@ -41,29 +41,23 @@ __device__ __forceinline__ void store8(uint8_t* p, uint32_t lo, uint32_t hi, boo
     }
 }
 
-template <typename SlotT, int MODE>
-__global__ __launch_bounds__(256) void kv_compress_epilog_kernel(EpilogParams a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (t >= a.num_tokens) return;
-    const int64_t s = (int64_t)static_cast<const SlotT*>(a.slots)[t];
-    if (s < 0 || s >= a.num_slots) return;
-    const int64_t blk = s / a.block_size, off = s - blk * a.block_size;
-    uint8_t* row = a.cache + blk * a.block_stride + off * a.head_dim;
+// One row: rope bytes, codes and scales of one token, whose first 512 nope
+// columns and rope the caller has loaded (lane l: columns 8l .. 8l + 7).
+template <int MODE>
+__device__ __forceinline__ void write_row(const EpilogParams& a, const uint16_t* xr, uint8_t* row, uint2 rope,
+                                          i32x4 raw0, int lane) {
     const bool al8 = (reinterpret_cast<uintptr_t>(row) & 7) == 0;
-    const uint16_t* xr = a.x + t * a.d;
     const int nope = a.d - 64;
-
-    if (lane < 16) {                                   // rope: the last 64 columns, as they are
-        const uint2 r = *reinterpret_cast<const uint2*>(xr + nope + 4 * lane);
-        store8(row + 8 * lane, r.x, r.y, al8);
-    }
+    if (lane < 16) store8(row + 8 * lane, rope.x, rope.y, al8);
     for (int base = 0; base < nope; base += 512) {
         const int c0 = base + 8 * lane;
         const bool act = c0 < nope;
         float v[8];
-        i32x4 raw = {0, 0, 0, 0};
-        if (act) raw = *reinterpret_cast<const i32x4*>(xr + c0);
+        i32x4 raw = raw0;
+        if (base > 0) {
+            raw = i32x4{0, 0, 0, 0};
+            if (act) raw = *reinterpret_cast<const i32x4*>(xr + c0);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = __uint_as_float((uint32_t)raw[i] << 16);
@@ -115,6 +109,26 @@ __global__ __launch_bounds__(256) void kv_compress_epilog_kernel(EpilogParams a)
             }
         }
     }
+}
+
+// The row's columns are requested together with its slot, not after the slot
+// test: the two memory round trips overlap (a skipped token's columns are read
+// for nothing, which costs less than a serial slot -> column chain per row).
+template <typename SlotT, int MODE>
+__global__ __launch_bounds__(256) void kv_compress_epilog_kernel(EpilogParams a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t >= a.num_tokens) return;
+    const int nope = a.d - 64;
+    const uint16_t* xr = a.x + t * a.d;
+    const int64_t s = (int64_t)static_cast<const SlotT*>(a.slots)[t];
+    uint2 rope = make_uint2(0u, 0u);
+    i32x4 raw = {0, 0, 0, 0};
+    if (lane < 16) rope = *reinterpret_cast<const uint2*>(xr + nope + 4 * lane);
+    if (8 * lane < nope) raw = *reinterpret_cast<const i32x4*>(xr + 8 * lane);
+    if (s < 0 || s >= a.num_slots) return;
+    const int64_t blk = s / a.block_size, off = s - blk * a.block_size;
+    write_row<MODE>(a, xr, a.cache + blk * a.block_stride + off * a.head_dim, rope, raw, lane);
 }
 
 hipError_t launch_kv_compress_epilog(const EpilogParams& p, int slot_bits, hipStream_t st) {

@@ -49,6 +49,8 @@ def _check(B, oracle_mod, inp, tag):
     (9, 128, 2, 8, 416, 0, 2),         # smallest d (one nope group)
     (6, 8192, 2, 4, 8576, 0, 1),       # largest d: 127 groups, 16 chunks of 512 columns
     (300, 576, 8, 64, 704, 0, 20),     # the MLA latent width (512 nope + 64 rope)
+    (37, 256, 5, 16, 357, 0, 4),       # odd head_dim in both modes: every row alignment mod 8
+    (50, 128, 4, 16, 227, 3, 5),       # odd head_dim and an odd gap between blocks; one scale piece
 ])
 def test_epilog_parity(B, oracle_mod, mode, round_scale, bits, shape):
     T, d, nb, bs, hd, pad, skip = shape
