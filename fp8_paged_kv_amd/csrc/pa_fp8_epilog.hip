@@ -12,9 +12,10 @@
 // offset * head_dim.
 //
 // Arithmetic: the scale is an fp32 division, mode 0 rounds it to bf16 (RNE) and
-// divides by the stored bf16 value, mode 1 by 2^k; quotients are fp32
-// divisions, clamped to +-448 and rounded to E4M3 (RNE) -- the codes are
-// decided in fp32, as on the page's vector unit.
+// divides by the stored bf16 value, mode 1 by 2^k (as a product with the exact
+// 2^-k, which rounds the same quotient once); quotients are fp32, clamped to
+// +-448 and rounded to E4M3 (RNE) -- the codes are decided in fp32, as on the
+// page's vector unit.
 //
 // Work: one wave per token.  Lane l handles 8 consecutive nope columns (one
 // 16-byte load); the 8 lanes of a 64-column group reduce its maximum with
@@ -70,7 +71,7 @@ __device__ __forceinline__ void write_row(const EpilogParams& a, const uint16_t*
         m = fmaxf(m, __shfl_xor(m, 2, 64));
         m = fmaxf(m, __shfl_xor(m, 4, 64));
         const float scale = m / 448.f;
-        float used;
+        float used, inv = 0.f;
         uint32_t sbits;
         if (MODE == 0) {
             const __bf16 sb = (__bf16)scale;
@@ -85,12 +86,15 @@ __device__ __forceinline__ void write_row(const EpilogParams& a, const uint16_t*
                 k = k < -127 ? -127 : (k > 127 ? 127 : k);
             }
             used = scale > 0.f ? ldexpf(1.f, k) : 0.f;
+            // k <= 120 (scale <= bf16 max / 448 < 2^120), so 2^-k is a normal float and
+            // x * 2^-k is the same correctly rounded number as x / 2^k, without a division
+            inv = scale > 0.f ? ldexpf(1.f, -k) : 0.f;
             sbits = (uint32_t)(k + 127);
         }
         float q[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float y = used > 0.f ? v[i] / used : 0.f;
+            const float y = MODE == 0 ? (used > 0.f ? v[i] / used : 0.f) : v[i] * inv;
             q[i] = fminf(fmaxf(y, -448.f), 448.f);
         }
         const uint32_t lo = cvt4_fp8(q[0], q[1], q[2], q[3]);

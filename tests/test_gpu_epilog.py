@@ -75,3 +75,25 @@ def test_epilog_full_size(B, oracle_mod):
     cfg = synth.EpilogConfig("epilog-bench", num_tokens=131072, d=576, block_num=1024, block_size=128,
                              head_dim=649, quant_mode=1, round_scale=True, seed=9)
     _check(B, oracle_mod, synth.make_epilog_inputs(cfg), "full size")
+
+
+@pytest.mark.parametrize("mode,round_scale", [(0, True), (1, True), (1, False)])
+def test_epilog_extreme_group_magnitudes(B, oracle_mod, mode, round_scale):
+    """Groups whose maxima sit at the ends of the bf16 range: at 2^-120 the fp32
+    scale is subnormal, the e8m0 exponent reaches its clamp at -127 and many
+    inputs are bf16 subnormals; at 2^126 the exponent reaches 119-120."""
+    d = 320
+    cfg = synth.EpilogConfig("extreme", num_tokens=16, d=d, block_num=2, block_size=16,
+                             head_dim=oracle_mod.kv_compress_cache_col(d, mode), quant_mode=mode,
+                             round_scale=round_scale, seed=5)
+    inp = synth.make_epilog_inputs(cfg)
+    x = inp["x"].double()
+    gains = [2.0 ** -120, 2.0 ** -100, 2.0 ** 100, 2.0 ** 126, 1.0]
+    for t in range(cfg.num_tokens):
+        for g in range(4):
+            grp = x[t, 64 * g:64 * g + 64]
+            amax = float(grp.abs().max())
+            if amax > 0:
+                x[t, 64 * g:64 * g + 64] = grp / amax * gains[(t + g) % len(gains)]
+    inp["x"] = x.to(torch.bfloat16)
+    _check(B, oracle_mod, inp, f"extreme magnitudes mode={mode} round={round_scale}")
