@@ -71,6 +71,9 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     static_assert(NCH >= 1 && (CL == 8 || CL == 4), "tile of at least 32 rows per wave");
 
     __shared__ int s_row[T];                                   // cache row of each tile position, -1 = past n
+    // byte offsets of that row (row 0 for -1) in the three planes, formed once per position:
+    // the gathers would otherwise redo a 64-bit multiply for every row they touch
+    __shared__ int64_t s_noff[T], s_roff[T], s_soff[T];
     __shared__ __attribute__((aligned(16))) uint8_t s_p[NB][2][64 * 16];   // BF16 P, MFMA A-operand layout
     __shared__ float s_max[NWV][kMlaHeads], s_sum[NWV][kMlaHeads];
     __shared__ __attribute__((aligned(16))) uint8_t s_qop[2][18][64 * 16];  // Q as MFMA B operands, per lane
@@ -112,6 +115,10 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
             row = id * kBlock + pos % kBlock;
         }
         s_row[i] = row;
+        const int64_t r = row < 0 ? 0 : row;
+        s_noff[i] = r * a.nope_stride;
+        s_roff[i] = r * a.rope_stride;
+        s_soff[i] = r * a.scale_stride;
     }
 
     // ---- query operands: heads h0 + 16 hh + lr; k-slot order shared with K ----------------
@@ -137,11 +144,10 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     struct KRows { f32x4 gs; i32x4 x[8]; i32x4 r0, r1; };
     KRows kq[3];
     auto issue_k = [&](int gq, KRows& kr) {
-        const int row = s_row[w * RW + 16 * gq + lr];     // this lane's K row (A operand row lr)
-        const int64_t r = row < 0 ? 0 : row;
-        const uint8_t* rp = a.nope + r * a.nope_stride;
-        const uint8_t* rrp = a.rope + r * a.rope_stride;
-        kr.gs = *reinterpret_cast<const f32x4*>(a.scales + r * a.scale_stride);
+        const int idx = w * RW + 16 * gq + lr;            // this lane's K row (A operand row lr)
+        const uint8_t* rp = a.nope + s_noff[idx];
+        const uint8_t* rrp = a.rope + s_roff[idx];
+        kr.gs = *reinterpret_cast<const f32x4*>(a.scales + s_soff[idx]);
 #pragma unroll
         for (int pr = 0; pr < 8; ++pr) kr.x[pr] = *reinterpret_cast<const i32x4*>(rp + 64 * pr + 16 * lg);
         kr.r0 = *reinterpret_cast<const i32x4*>(rrp + 32 * lg);
@@ -232,9 +238,9 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
         neg = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int row = s_row[32 * bi + chunk_token(lg, j)];
-            const int64_t r = row < 0 ? 0 : row;
-            const uint8_t* vp = a.nope + r * a.nope_stride + CPW * w + CL * lr;
+            const int idx = 32 * bi + chunk_token(lg, j);
+            const int row = s_row[idx];
+            const uint8_t* vp = a.nope + s_noff[idx] + CPW * w + CL * lr;
             if (CL == 8) {
                 const uint2 v2 = *reinterpret_cast<const uint2*>(vp);
                 x[j][0] = v2.x;
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
             } else {
                 x[j][0] = *reinterpret_cast<const uint32_t*>(vp);
             }
-            sc[j] = *reinterpret_cast<const float*>(a.scales + r * a.scale_stride + 4 * grp);
+            sc[j] = *reinterpret_cast<const float*>(a.scales + s_soff[idx] + 4 * grp);
             neg |= (row < 0) << j;
         }
     };
