@@ -130,11 +130,15 @@ def cpu_baseline(cfg, sets, seqs, target_s):
     dt = time.perf_counter() - t0
     sub = synth.GqaConfig(**{**cfg.__dict__, "B": nb})
     sample_bytes = synth.gqa_algorithmic_bytes(sub, seqs[:nb])
+    one_bytes = synth.gqa_algorithmic_bytes(synth.GqaConfig(**{**cfg.__dict__, "B": 1}), seqs[:1])
     full_tokens = sum(seqs)
     return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
             "sample": f"sequences 0..{nb - 1} of {cfg.B} ({sum(seqs[:nb])} of {full_tokens} tokens, all "
                       f"{cfg.nq} query heads), FP64 C oracle, {dt:.2f} s wall on {used} threads",
-            "calls_per_s_equiv": round((sum(seqs[:nb]) / full_tokens) / dt, 6)}
+            "calls_per_s_equiv": round((sum(seqs[:nb]) / full_tokens) / dt, 6),
+            "single_thread": {"value": round(one_bytes / one / 1e9, 4), "unit": "GB/s",
+                              "sample": f"sequence 0 ({seqs[0]} tokens, all {cfg.nq} query heads), 1 thread, "
+                                        f"{one:.2f} s wall"}}
 
 
 def pmc_traffic():

@@ -38,3 +38,19 @@ def test_algorithmic_bytes_of_the_benchmark_workload():
     # the K / V / k_scale part equals the bytes of those tensors the valid tokens occupy
     k_rows = int(torch.tensor(seqs).sum()) * cfg.nkv * cfg.D
     assert tokens * per_token == 2 * k_rows + 4 * tokens * cfg.nkv
+
+
+def test_cpu_baseline_fields_on_the_small_workload():
+    """The oracle leg as bench.py reports it, on the small two-sequence workload:
+    a multi-thread figure over a bounded sample and the single-thread one."""
+    sys.path.insert(0, ROOT)
+    import bench
+    cfg = synth.CONFIGS[0]
+    inp = synth.make_gqa_inputs(cfg)
+    seqs = inp["kv_act_seqs"].tolist()
+    r = bench.cpu_baseline(cfg, [inp], seqs, target_s=5.0)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= 16
+    assert "sequences 0..1 of 2" in r["sample"]                       # both sequences fit the budget
+    st = r["single_thread"]
+    assert st["value"] > 0 and "1 thread" in st["sample"] and f"{seqs[0]} tokens" in st["sample"]
