@@ -252,6 +252,13 @@ def main():
                      "kernel": ("pa::decode_rows_kernel + pa::merge_rows_kernel" if args.splits == 0
                                 else "pa::decode_kernel" + (" + pa::combine_kernel" if nsplit > 1 else ""))},
     }
+    # secondary: the two contractions (S = Q K^T and P V) as bf16 MFMA work on exact FP8 codes
+    flops = 4 * cfg.D * cfg.s1 * cfg.nq * sum(seqs)
+    line["mfma_secondary"] = {
+        "flop_per_call": flops, "achieved": round(flops / (region * 1e-3) / 1e12, 2), "peak": 2500.0,
+        "unit": "TFLOP/s", "frac": round(flops / (region * 1e-3) / 1e12 / 2500.0, 4),
+        "note": "analytic, exact lengths; the work executed with query rows padded to 16 is counted by "
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16 in profiles/mfma_counters_glm45_b32_and_mla.md"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, sets, seqs, args.cpu_target_s)
     print(json.dumps(line), flush=True)
