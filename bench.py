@@ -252,6 +252,11 @@ def main():
                      "kernel": ("pa::decode_rows_kernel + pa::merge_rows_kernel" if args.splits == 0
                                 else "pa::decode_kernel" + (" + pa::combine_kernel" if nsplit > 1 else ""))},
     }
+    # over-fetch by whole cache blocks: a sequence's last block is read in full (masked past its length)
+    blk_tokens = sum((sq + cfg.block_size - 1) // cfg.block_size * cfg.block_size for sq in seqs)
+    block_bytes = nbytes + (blk_tokens - sum(seqs)) * cfg.nkv * (2 * cfg.D + 4)
+    line["block_granular"] = {"bytes_per_call": block_bytes, "ratio_to_algorithmic": round(block_bytes / nbytes, 4),
+                              "gb_s": round(block_bytes / (region * 1e-3) / 1e9, 2)}
     # secondary: the two contractions (S = Q K^T and P V) as bf16 MFMA work on exact FP8 codes
     flops = 4 * cfg.D * cfg.s1 * cfg.nq * sum(seqs)
     line["mfma_secondary"] = {
@@ -300,6 +305,9 @@ def run_mla(args):
                      "unit": "TFLOP/s", "frac": round(flops / (mean * 1e-3) / 1e12 / 2500.0, 4), "traffic": None,
                      "hbm_gb_s": round(nbytes / (mean * 1e-3) / 1e9, 1),
                      "kernel": "pa::mla_decode_kernel + pa::mla_merge_kernel"},
+        # a gathered row is 656 used bytes of a 672-byte cache row
+        "row_stride": {"bytes_per_call": nbytes + ntok * (672 - 656),
+                       "ratio_to_algorithmic": round((nbytes + ntok * (672 - 656)) / nbytes, 4)},
     }
     print(json.dumps(line), flush=True)
 
