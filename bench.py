@@ -45,6 +45,10 @@ def parse_args():
                     help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
                          "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows")
     ap.add_argument("--splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--causal", action="store_true",
+                    help="GQA: causal multi-token decode (position s of s1 sees the first seq - s1 + 1 + s tokens)")
+    ap.add_argument("--kv-split", action="store_true",
+                    help="config 4: the MLA cache as three tensors (codes, rope, scales) instead of 672-byte rows")
     ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled by the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-target-s", type=float, default=15.0, help="wall seconds budget of the oracle sample")
@@ -176,6 +180,11 @@ def main():
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
     sets, seqs = make_sets(cfg, max(1, args.rotate))
+    if args.causal:
+        if args.splits:
+            sys.exit("--causal runs on the whole-row path (--splits 0)")
+        for st in sets:
+            st["causal"] = True
     nbytes = synth.gqa_algorithmic_bytes(cfg, seqs)
     kv_bytes = sum(seqs) * cfg.nkv * 2 * cfg.D
     out = torch.empty((cfg.B * cfg.s1, cfg.nq, cfg.D), dtype=torch.bfloat16, device="cuda")
@@ -235,6 +244,7 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "s1": cfg.s1, "nq": cfg.nq, "nkv": cfg.nkv, "D": cfg.D,
                    "block_size": cfg.block_size, "s2_tile": cfg.s2_tile, "seq_lens": "U[1024,8192] seed 1",
                    "total_tokens": sum(seqs), "path": "whole-row" if args.splits == 0 else f"per-head, {nsplit} splits",
+                   "causal": bool(args.causal),
                    "rotating_input_sets": len(sets),
                    "algorithmic_bytes_per_call": nbytes},
         "calls_per_s": round(1.0 / (ms_per_step * 1e-3), 1),
@@ -281,8 +291,12 @@ def run_mla(args):
     out = torch.empty((cfg.B * cfg.s1 * cfg.nq, 512), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(binding.mla_workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
                      device="cuda")
+    if args.kv_split:
+        sets = [synth.mla_kv_split(st) for st in sets]
+    run_one = binding.mla_decode_kv_split_inputs if args.kv_split else binding.mla_decode_inputs
+
     def call(i, stream):
-        binding.mla_decode_inputs(sets[i % len(sets)], out=out, workspace=ws, stream=stream)
+        run_one(sets[i % len(sets)], out=out, workspace=ws, stream=stream)
 
     wall, region, ev = _timed(call, args.steps, args.warmup)
     nbytes = synth.mla_algorithmic_bytes(cfg, seqs)
@@ -296,7 +310,8 @@ def run_mla(args):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 MFMA on dequantised fp8 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "s1": cfg.s1, "nq": cfg.nq, "topk": cfg.topk,
-                   "s2_tile": cfg.s2_tile, "algorithmic_bytes_per_call": nbytes, "flop_per_call": flops},
+                   "s2_tile": cfg.s2_tile, "algorithmic_bytes_per_call": nbytes, "flop_per_call": flops,
+                   "layout": "kv_split (three tensors)" if args.kv_split else "packed 672-byte rows"},
         "event_us_per_call_timed_region": round(region * 1e3, 2),
         "event_us_per_call": {"mean": round(sum(ev) / len(ev) * 1e3, 2), "median": round(ev[len(ev) // 2] * 1e3, 2),
                               "note": "separate pass, one event pair around each call"},
