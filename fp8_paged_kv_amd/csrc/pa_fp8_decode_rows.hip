@@ -180,7 +180,11 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     const int64_t C = lds_uniform(&s_pref[BV]);
     const int U = lds_uniform(&s_units);
     const int Geff = min((int)gridDim.x, U);
-    const int g = blockIdx.x;
+    // workgroups are dispatched round-robin over the 8 XCDs: neighbouring ranges (usually
+    // the head groups of one sequence, which read the same k_scale sectors and table row)
+    // go to one XCD so that they share its L2
+    const int G8 = (int)gridDim.x / 8;
+    const int g = ((int)gridDim.x % 8 == 0) ? ((int)blockIdx.x % 8) * G8 + (int)blockIdx.x / 8 : (int)blockIdx.x;
 
     if (g == 0) {
         // the partition, for the merge kernel: cost prefix over (batch, group), then Geff
