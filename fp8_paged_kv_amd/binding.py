@@ -22,7 +22,7 @@ EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug
            "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode",
            "pa_fp8_mla_sparse_decode_kv_split", "pa_fp8_scatter_kv_cache",
            "pa_fp8_kv_compress_epilog_workspace_size", "pa_fp8_kv_compress_epilog",
-           "pa_fp8_last_error", "pa_fp8_version")
+           "pa_fp8_last_error_string", "pa_fp8_last_error", "pa_fp8_version")
 
 PA_CACHE_BSND, PA_CACHE_BNBD = 0, 1
 
@@ -55,9 +55,9 @@ def lib():
         L.pa_fp8_decode_workspace_size.restype = I
         L.pa_fp8_mla_workspace_size.argtypes = [I] * 5 + [P]
         L.pa_fp8_mla_workspace_size.restype = I
-        L.pa_fp8_mla_sparse_decode.argtypes = [P] * 7 + [I] * 7 + [F, I, P, Z, P]
+        L.pa_fp8_mla_sparse_decode.argtypes = [P] * 7 + [I] * 8 + [F, I, P, Z, P]
         L.pa_fp8_mla_sparse_decode.restype = I
-        L.pa_fp8_mla_sparse_decode_kv_split.argtypes = [P] * 9 + [I] * 7 + [F, I, P, Z, P]
+        L.pa_fp8_mla_sparse_decode_kv_split.argtypes = [P] * 9 + [I] * 8 + [F, I, P, Z, P]
         L.pa_fp8_mla_sparse_decode_kv_split.restype = I
         L.pa_fp8_scatter_kv_cache.argtypes = [P] * 7 + [I] * 8 + [ctypes.c_int64] * 4 + [P]
         L.pa_fp8_scatter_kv_cache.restype = I
@@ -65,6 +65,8 @@ def lib():
         L.pa_fp8_kv_compress_epilog_workspace_size.restype = I
         L.pa_fp8_kv_compress_epilog.argtypes = [P] * 3 + [I] * 5 + [ctypes.c_int64] + [I] * 4 + [F, P, Z, P]
         L.pa_fp8_kv_compress_epilog.restype = I
+        L.pa_fp8_last_error_string.argtypes = []
+        L.pa_fp8_last_error_string.restype = ctypes.c_char_p
         L.pa_fp8_last_error.argtypes = []
         L.pa_fp8_last_error.restype = ctypes.c_char_p
         L.pa_fp8_version.argtypes = []
@@ -75,7 +77,7 @@ def lib():
 
 def _check(rc: int):
     if rc != PA_OK:
-        raise PaError(rc, lib().pa_fp8_last_error().decode())
+        raise PaError(rc, lib().pa_fp8_last_error_string().decode())
 
 
 def _ptr(t):
@@ -181,11 +183,11 @@ def mla_workspace_size(B, s1, nq, topk, s2_tile):
 
 
 def mla_decode(q_nope, q_rope, cache, topk, block_table, kv_act_seqs, softmax_scale, s2_tile, s1,
-               out=None, workspace=None, stream=None, block_size=128):
-    """MLA sparse decode; returns out [B*s1*nq, 512] bf16 (allocated if not given)."""
+               out=None, workspace=None, stream=None, block_size=128, nkv=1):
+    """MLA sparse decode; topk [B*s1, nkv*topk]; returns out [B*s1*nq, 512] bf16 (allocated if not given)."""
     B = int(kv_act_seqs.shape[0])
     nq = int(q_nope.shape[0]) // (B * s1)
-    K = int(topk.shape[1])
+    K = int(topk.shape[1]) // nkv
     _checked_inputs(dict(q_nope=q_nope, q_rope=q_rope, cache=cache, topk=topk, block_table=block_table,
                          kv_act_seqs=kv_act_seqs, out=out, workspace=workspace))
     if out is None:
@@ -195,19 +197,19 @@ def mla_decode(q_nope, q_rope, cache, topk, block_table, kv_act_seqs, softmax_sc
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
     _check(lib().pa_fp8_mla_sparse_decode(
         _ptr(q_nope), _ptr(q_rope), _ptr(cache), _ptr(topk), _ptr(block_table), _ptr(kv_act_seqs), _ptr(out),
-        B, s1, nq, K, block_size, int(block_table.shape[1]), int(cache.shape[0]) // block_size,
+        B, s1, nq, nkv, K, block_size, int(block_table.shape[1]), int(cache.shape[0]) // block_size,
         float(softmax_scale), int(s2_tile), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
 
 
 def mla_decode_kv_split(q_nope, q_rope, kn_quant, kr, kn_scales, topk, block_table, kv_act_seqs, softmax_scale,
-                        s2_tile, s1, out=None, workspace=None, stream=None, block_size=128):
+                        s2_tile, s1, out=None, workspace=None, stream=None, block_size=128, nkv=1):
     """MLA sparse decode over the kv_split cache (kn_quant [rows, 512] uint8,
     kr [rows, 64] bf16, kn_scales [rows, 4] float32); returns out [B*s1*nq, 512] bf16."""
     B = int(kv_act_seqs.shape[0])
     nq = int(q_nope.shape[0]) // (B * s1)
-    K = int(topk.shape[1])
+    K = int(topk.shape[1]) // nkv
     _checked_inputs(dict(q_nope=q_nope, q_rope=q_rope, kn_quant=kn_quant, kr=kr, kn_scales=kn_scales, topk=topk,
                          block_table=block_table, kv_act_seqs=kv_act_seqs, out=out, workspace=workspace))
     if kn_quant.shape[1] != 512 or kr.shape[1] != 64 or kn_scales.shape[1] != 4:
@@ -219,7 +221,7 @@ def mla_decode_kv_split(q_nope, q_rope, kn_quant, kr, kn_scales, topk, block_tab
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
     _check(lib().pa_fp8_mla_sparse_decode_kv_split(
         _ptr(q_nope), _ptr(q_rope), _ptr(kn_quant), _ptr(kr), _ptr(kn_scales), _ptr(topk), _ptr(block_table),
-        _ptr(kv_act_seqs), _ptr(out), B, s1, nq, K, block_size, int(block_table.shape[1]),
+        _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, K, block_size, int(block_table.shape[1]),
         int(kn_quant.shape[0]) // block_size, float(softmax_scale), int(s2_tile), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
@@ -231,7 +233,7 @@ def mla_decode_kv_split_inputs(inp: dict, out=None, workspace=None, stream=None)
     return mla_decode_kv_split(inp["q_nope"], inp["q_rope"], inp["kn_quant"], inp["kr"], inp["kn_scales"],
                                inp["topk"], inp["block_table"], inp["kv_act_seqs"], inp["softmax_scale"],
                                inp.get("s2_tile", cfg.s2_tile), cfg.s1, out=out, workspace=workspace,
-                               stream=stream, block_size=cfg.block_size)
+                               stream=stream, block_size=cfg.block_size, nkv=cfg.nkv)
 
 
 def mla_decode_inputs(inp: dict, out=None, workspace=None, stream=None):
@@ -239,7 +241,7 @@ def mla_decode_inputs(inp: dict, out=None, workspace=None, stream=None):
     cfg = inp["cfg"]
     return mla_decode(inp["q_nope"], inp["q_rope"], inp["cache"], inp["topk"], inp["block_table"],
                       inp["kv_act_seqs"], inp["softmax_scale"], inp.get("s2_tile", cfg.s2_tile), cfg.s1,
-                      out=out, workspace=workspace, stream=stream, block_size=cfg.block_size)
+                      out=out, workspace=workspace, stream=stream, block_size=cfg.block_size, nkv=cfg.nkv)
 
 
 def scatter_kv_cache(key, value, key_cache, value_cache, slot_mapping, key_scale, key_scale_cache,

@@ -215,14 +215,20 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
 pa_status_t run_mla(const void* q_nope, const void* q_rope, const uint8_t* nope, const uint8_t* rope,
                     const uint8_t* scales, int64_t nope_stride, int64_t rope_stride, int64_t scale_stride,
                     const int32_t* topk_dev, const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
-                    void* out_dev, int B, int s1, int nq, int topk, int block_size, int max_blocks_per_seq,
-                    int num_blocks, float softmax_scale, int s2_tile, void* workspace_dev, size_t workspace_bytes,
-                    void* stream) {
+                    void* out_dev, int B, int s1, int nq, int nkv, int topk, int block_size,
+                    int max_blocks_per_seq, int num_blocks, float softmax_scale, int s2_tile, void* workspace_dev,
+                    size_t workspace_bytes, void* stream) {
     if (!q_nope || !q_rope || !topk_dev || !block_table_dev || !kv_act_seqs_dev || !out_dev)
         return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
     size_t need = 0;
     pa_status_t st = pa_fp8_mla_workspace_size(B, s1, nq, topk, s2_tile, &need);
     if (st != PA_OK) return st;
+    if (nkv <= 0 || nq % nkv != 0)
+        return fail(PA_ERR_INVALID, "nkv (%d) must be positive and divide nq (%d)", nkv, nq);
+    if (!pa::mla_supported(nq, nkv, s2_tile))
+        return fail(PA_ERR_UNSUPPORTED, "MLA decode built for nq / nkv a multiple of 32 (nq=%d nkv=%d)", nq, nkv);
+    if ((int64_t)B * s1 * nkv * topk > ((int64_t)1 << 31) - 1)
+        return fail(PA_ERR_UNSUPPORTED, "B * s1 * nkv * topk exceeds 2^31 - 1 indices");
     if (block_size != pa::kBlock)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (only 128)", block_size);
     if (max_blocks_per_seq <= 0 || num_blocks <= 0)
@@ -262,6 +268,7 @@ pa_status_t run_mla(const void* q_nope, const void* q_rope, const uint8_t* nope,
     p.B = B;
     p.s1 = s1;
     p.nq = nq;
+    p.nkv = nkv;
     p.topk = topk;
     p.max_blocks = max_blocks_per_seq;
     p.num_blocks = num_blocks;
@@ -336,9 +343,8 @@ pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_ti
     if (B <= 0 || s1 <= 0 || nq <= 0 || topk <= 0 || s2_tile <= 0)
         return fail(PA_ERR_INVALID, "sizes must be positive (B=%d s1=%d nq=%d topk=%d s2_tile=%d)", B, s1, nq,
                     topk, s2_tile);
-    if (!pa::mla_supported(nq, s2_tile))
-        return fail(PA_ERR_UNSUPPORTED, "MLA decode built for nq a multiple of 32 and s2_tile 128/256/512 "
-                    "(nq=%d s2_tile=%d)", nq, s2_tile);
+    if (s2_tile != 128 && s2_tile != 256 && s2_tile != 512)
+        return fail(PA_ERR_UNSUPPORTED, "MLA decode built for s2_tile 128/256/512 (s2_tile=%d)", s2_tile);
     const size_t rows = (size_t)B * s1 * nq, nt = (size_t)((topk + s2_tile - 1) / s2_tile);
     *bytes_host = align256(rows * nt * 2 * sizeof(float)) + rows * nt * 512 * sizeof(float);
     return PA_OK;
@@ -347,13 +353,13 @@ pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_ti
 pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_dev, const uint8_t* cache_dev,
                                      const int32_t* topk_dev, const int32_t* block_table_dev,
                                      const int32_t* kv_act_seqs_dev, void* out_dev, int B, int s1, int nq,
-                                     int topk, int block_size, int max_blocks_per_seq, int num_blocks,
+                                     int nkv, int topk, int block_size, int max_blocks_per_seq, int num_blocks,
                                      float softmax_scale, int s2_tile, void* workspace_dev,
                                      size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (!cache_dev) return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
     return run_mla(q_nope_dev, q_rope_dev, cache_dev, cache_dev + 512, cache_dev + 640, 672, 672, 672, topk_dev,
-                   block_table_dev, kv_act_seqs_dev, out_dev, B, s1, nq, topk, block_size, max_blocks_per_seq,
+                   block_table_dev, kv_act_seqs_dev, out_dev, B, s1, nq, nkv, topk, block_size, max_blocks_per_seq,
                    num_blocks, softmax_scale, s2_tile, workspace_dev, workspace_bytes, stream);
 }
 
@@ -361,15 +367,15 @@ pa_status_t pa_fp8_mla_sparse_decode_kv_split(const void* q_nope_dev, const void
                                               const uint8_t* kn_quant_dev, const void* kr_dev,
                                               const float* kn_scales_dev, const int32_t* topk_dev,
                                               const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
-                                              void* out_dev, int B, int s1, int nq, int topk, int block_size,
-                                              int max_blocks_per_seq, int num_blocks, float softmax_scale,
-                                              int s2_tile, void* workspace_dev, size_t workspace_bytes,
-                                              void* stream) {
+                                              void* out_dev, int B, int s1, int nq, int nkv, int topk,
+                                              int block_size, int max_blocks_per_seq, int num_blocks,
+                                              float softmax_scale, int s2_tile, void* workspace_dev,
+                                              size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (!kn_quant_dev || !kr_dev || !kn_scales_dev) return fail(PA_ERR_NULLPTR, "a required pointer is NULL");
     return run_mla(q_nope_dev, q_rope_dev, kn_quant_dev, static_cast<const uint8_t*>(kr_dev),
                    reinterpret_cast<const uint8_t*>(kn_scales_dev), 512, 128, 16, topk_dev, block_table_dev,
-                   kv_act_seqs_dev, out_dev, B, s1, nq, topk, block_size, max_blocks_per_seq, num_blocks,
+                   kv_act_seqs_dev, out_dev, B, s1, nq, nkv, topk, block_size, max_blocks_per_seq, num_blocks,
                    softmax_scale, s2_tile, workspace_dev, workspace_bytes, stream);
 }
 
@@ -488,6 +494,8 @@ pa_status_t pa_fp8_kv_compress_epilog(uint8_t* cache_dev, const void* x_dev, con
     if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
     return PA_OK;
 }
+
+const char* pa_fp8_last_error_string(void) { return g_err; }
 
 const char* pa_fp8_last_error(void) { return g_err; }
 

@@ -42,13 +42,13 @@ struct MlaParams {
     const uint8_t* rope;        // row r: 64 bf16 at rope + r * rope_stride
     const uint8_t* scales;      // row r: 4 fp32 group scales at scales + r * scale_stride
     int64_t nope_stride, rope_stride, scale_stride;   // bytes
-    const int32_t* topk_idx;    // [B*s1, topk] logical token positions
+    const int32_t* topk_idx;    // [B*s1, nkv*topk] logical token positions, one slice per KV head
     const int32_t* block_table; // [B, max_blocks]
     const int32_t* seqs;        // [B]
     uint16_t* out;              // [B*s1*nq, 512] bf16
     float* part_o;              // [B*s1*nq, ntiles_max, 512]
     float* part_ml;             // [B*s1*nq, ntiles_max, 2]  (tile max in log2 units, sum)
-    int B, s1, nq, topk, max_blocks, num_blocks, capacity, s2_tile, ntiles_max;
+    int B, s1, nq, nkv, topk, max_blocks, num_blocks, capacity, s2_tile, ntiles_max;
     float softmax_scale;
 };
 
@@ -78,7 +78,7 @@ struct EpilogParams {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, bool debug);
 hipError_t launch_kv_compress_epilog(const EpilogParams& p, int slot_bits, hipStream_t stream);
 hipError_t launch_scatter_kv(const ScatterParams& p, int slot_bits, int layout, hipStream_t stream);
-bool mla_supported(int nq, int s2_tile);
+bool mla_supported(int nq, int nkv, int s2_tile);
 hipError_t launch_mla(const MlaParams& p, hipStream_t stream);
 int grid_size(const DecodeParams& p);
 bool rows_path_supported(int nkv, int s2_tile, int rows, int s1, int nq, int B);

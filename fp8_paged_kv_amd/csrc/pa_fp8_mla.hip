@@ -96,6 +96,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     }
     const int t = rest % a.ntiles_max, bs = rest / a.ntiles_max;
     const int b = bs / a.s1, s = bs - b * a.s1;
+    const int kvh = hb * kMlaHeads / (a.nq / a.nkv);         // the KV head (top-k slice) of these heads
 
     int seq = a.seqs[b];
     seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
         const int j = t * T + i;
         int row = -1;
         if (j < n) {
-            int pos = a.topk_idx[(int64_t)bs * a.topk + j];
+            int pos = a.topk_idx[((int64_t)bs * a.nkv + kvh) * a.topk + j];
             pos = pos < 0 ? 0 : (pos >= seq ? seq - 1 : pos);
             int id = a.block_table[(int64_t)b * a.max_blocks + pos / kBlock];
             id = (id < 0 || id >= a.num_blocks) ? 0 : id;
@@ -248,7 +249,10 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
             } else {
                 x[j][0] = *reinterpret_cast<const uint32_t*>(vp);
             }
-            sc[j] = *reinterpret_cast<const float*>(a.scales + s_soff[idx] + 4 * grp);
+            // a position past n reads row 0, whose scale may be NaN / Inf: use 0 so that
+            // its zeroed codes dequantise to 0 and P = 0 multiplies a finite value
+            const float scv = *reinterpret_cast<const float*>(a.scales + s_soff[idx] + 4 * grp);
+            sc[j] = row < 0 ? 0.f : scv;
             neg |= (row < 0) << j;
         }
     };
@@ -362,8 +366,10 @@ static hipError_t launch_mla_t(const MlaParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-bool mla_supported(int nq, int s2_tile) {
-    return nq % kMlaHeads == 0 && (s2_tile == 128 || s2_tile == 256 || s2_tile == 512);
+// query heads of one KV head come in whole blocks of 32 (a workgroup reads one top-k slice)
+bool mla_supported(int nq, int nkv, int s2_tile) {
+    return nkv >= 1 && nq % nkv == 0 && (nq / nkv) % kMlaHeads == 0 &&
+           (s2_tile == 128 || s2_tile == 256 || s2_tile == 512);
 }
 
 hipError_t launch_mla(const MlaParams& p, hipStream_t st) {

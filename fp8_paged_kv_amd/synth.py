@@ -92,10 +92,7 @@ class MlaConfig:
     s2_tile: int = 512
     seed: int = 4
     seq_lens: Optional[Sequence[int]] = None
-
-    @property
-    def nkv(self) -> int:
-        return 1
+    nkv: int = 1                               # KV heads, each with its own top-k slice
 
     @property
     def softmax_scale(self) -> float:
@@ -278,9 +275,10 @@ def make_mla_inputs(cfg: MlaConfig, device="cpu", seed: Optional[int] = None,
     Recipe: query nope/rope ~ N(0,1) rounded to bf16; per cache row the 512
     nope values ~ N(0,1) are quantised per 128-channel group with scale =
     amax/448 (torch's e4m3 cast), the 64 rope values ~ N(0,1) are stored as
-    bf16; top-k indices per query token are drawn uniformly without
-    replacement from [0, seq) (all of [0, seq) when seq <= topk, followed by
-    -1 padding).
+    bf16; top-k indices per query token and KV head are drawn uniformly
+    without replacement from [0, seq) (all of [0, seq) when seq <= topk,
+    followed by -1 padding); topk is [B*s1, nkv*topk], KV head h's slice at
+    columns [h*topk, (h+1)*topk).
     """
     seed = cfg.seed if seed is None else seed
     if seq_lens is not None:
@@ -304,19 +302,18 @@ def make_mla_inputs(cfg: MlaConfig, device="cpu", seed: Optional[int] = None,
     cache[:, 640:656] = gscale.contiguous().view(torch.uint8).view(nrows, 16)
     del kn
 
-    topk = torch.full((B * s1, cfg.topk), -1, dtype=torch.int32)
+    K = cfg.topk
+    topk = torch.full((B * s1, cfg.nkv * K), -1, dtype=torch.int32)
     for b in range(B):
         sq = int(seqs[b])
         for s in range(s1):
-            n = min(sq, cfg.topk)
+            n = min(sq, K)
             if n == 0:
                 continue
-            if sq <= cfg.topk:
-                sel = torch.randperm(sq, generator=g, device=device)[:n]
-            else:
+            for h in range(cfg.nkv):
                 # uniform without replacement: first n of a random permutation
                 sel = torch.randperm(sq, generator=g, device=device)[:n]
-            topk[b * s1 + s, :n] = sel.cpu().to(torch.int32)
+                topk[b * s1 + s, h * K:h * K + n] = sel.cpu().to(torch.int32)
 
     return dict(
         cfg=cfg,
@@ -363,7 +360,7 @@ def mla_algorithmic_bytes(cfg: MlaConfig, seqs: Sequence[int]) -> int:
     address them, the bf16 queries (576 values) and bf16 outputs (512)."""
     n = 0
     for s in seqs:
-        n += cfg.s1 * min(int(s), cfg.topk)
+        n += cfg.s1 * cfg.nkv * min(int(s), cfg.topk)
     rows = cfg.B * cfg.s1 * cfg.nq
     return n * (656 + 4 + 4) + rows * (MLA_NOPE + MLA_ROPE) * 2 + rows * MLA_NOPE * 2 + 4 * cfg.B
 

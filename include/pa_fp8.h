@@ -35,7 +35,7 @@
  *    zero-filled); every call leaves them zero again.
  *  - Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and a status != PA_OK is returned, with a
- *    message available from pa_fp8_last_error() (per host thread).
+ *    message available from pa_fp8_last_error_string() (per host thread).
  *  - Scales are dequantisation multipliers (amax / 448): a value is
  *    code_value * scale.  [P1] stores 448 / amax and dequantises with its
  *    reciprocal; the two are the same scale.
@@ -106,11 +106,22 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
  * [0, max_blocks_per_seq * block_size]; seq_b == 0 gives zero output rows;
  * bytes of tokens p >= seq_b are never used (their values may be NaN).
  * Supported: D == 128, block_size == 128, s2_tile in {128, 256, 512, 1024,
- * 2048}, s1 * nq / nkv <= 64.  num_splits: 0 = the library's choice (a
- * balanced split of the whole batch across the GPU when the shape allows
- * it), else the number of contiguous tile ranges each sequence is split
- * into (>= 1).  Whenever pa_fp8_decode_workspace_size reports a nonzero
- * size, workspace_dev must hold at least that many bytes.
+ * 2048}, s1 * nq / nkv <= 64.  num_splits: 0 = the library's choice, else
+ * the number of contiguous tile ranges each sequence is split into (>= 1).
+ * Whenever pa_fp8_decode_workspace_size reports a nonzero size,
+ * workspace_dev must hold at least that many bytes.
+ * Two kernels serve the call (same results within the stated tolerance):
+ *  - num_splits == 0 and the shape inside the whole-row path's limits: one
+ *    workgroup per CU streams a cost-balanced range of (batch, KV-head pair,
+ *    tile) units and a small second kernel merges split sequences.  Limits:
+ *    s1 * nq / nkv <= 32 query rows per KV head (<= 16 with s2_tile 1024;
+ *    s2_tile 2048 is not served) and B * ceil(nkv / 2) <= 1024 (batch, head
+ *    pair) units (nkv odd: B * nkv <= 1024).
+ *  - otherwise (an explicit num_splits, or a shape outside those limits,
+ *    e.g. B >= 257 at nkv = 8): one workgroup per (batch, KV head, split)
+ *    with the split count chosen from the table capacity.  It is the slower
+ *    path for large batches of short sequences; choose shapes inside the
+ *    whole-row limits where speed matters.
  */
 pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev,
                           const uint8_t* k_cache_dev, const float* k_scale_dev,
@@ -165,11 +176,14 @@ pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_ti
 
 /*
  * MLA-style sparse attention decode over an FP8 latent cache, [P2] sections
- * 核心参数与 KV Cache 布局, 计算流程, 关键实现细节 and 在线反量化与 Online Softmax.
- * One latent KV head shared by all nq query heads.  For batch b and query
- * position s < s1, the first n = clamp(seq_b - s1 + 1 + s, 0, topk) entries
- * of topk_dev[b*s1 + s] are logical token positions (clamped to [0, seq_b));
- * position p reads cache row block_table[b, p / 128] * 128 + p % 128.
+ * 核心参数与 KV Cache 布局, API 签名, 计算流程, 关键实现细节 and 在线反量化与
+ * Online Softmax.  nkv KV heads read the same latent rows, each through its
+ * own top-k slice: query head qh uses KV head h = qh / (nq / nkv) and the
+ * indices topk_dev[b*s1 + s, h*topk .. h*topk + topk) ([P2]'s
+ * topk_indices (t, n_kv*topk)).  For batch b and query position s < s1, the
+ * first n = clamp(seq_b - s1 + 1 + s, 0, topk) entries of a slice are
+ * logical token positions (each clamped to [0, seq_b)); position p reads
+ * cache row block_table[b, p / 128] * 128 + p % 128.
  *   kn[c] = bf16(fp32(e4m3(row[c]) * scale[c / 128]))   c < 512 (row bytes 0..511,
  *           scales = FP32 at bytes 640..655)
  *   kr    = the 64 BF16 values at row bytes 512..639;  K = [kn | kr], V = kn
@@ -179,17 +193,22 @@ pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_ti
  * Layouts:
  *   q_nope_dev   [B*s1*nq, 512] bf16      q_rope_dev [B*s1*nq, 64] bf16
  *   cache_dev    [num_blocks*128, 672] bytes (one row per token slot)
- *   topk_dev     [B*s1, topk] int32       block_table_dev [B, max_blocks_per_seq] int32
+ *   topk_dev     [B*s1, nkv*topk] int32   block_table_dev [B, max_blocks_per_seq] int32
  *   kv_act_seqs_dev [B] int32             out_dev [B*s1*nq, 512] bf16 (written completely)
  * Device-side rules as for pa_fp8_decode (ids < 0 or >= num_blocks read block
- * 0; seq clamped to the table capacity).  Supported: block_size 128, nq a
- * multiple of 32, s2_tile 128 / 256 / 512.  The workspace (size from
- * pa_fp8_mla_workspace_size) holds per-tile partial results.
+ * 0; seq clamped to the table capacity); only the first n entries of a
+ * slice are read, and bytes of rows they do not select are never used
+ * (they may hold NaN codes and scales).  Host checks: NULL pointers
+ * (PA_ERR_NULLPTR); sizes > 0, nq % nkv == 0, finite softmax_scale > 0
+ * (PA_ERR_INVALID); block_size 128, nq / nkv a multiple of 32, s2_tile
+ * 128 / 256 / 512, 16-byte aligned queries, cache planes and output
+ * (PA_ERR_UNSUPPORTED).  The workspace (size from pa_fp8_mla_workspace_size)
+ * holds per-tile partial results.
  */
 pa_status_t pa_fp8_mla_sparse_decode(const void* q_nope_dev, const void* q_rope_dev, const uint8_t* cache_dev,
                                      const int32_t* topk_dev, const int32_t* block_table_dev,
                                      const int32_t* kv_act_seqs_dev, void* out_dev, int B, int s1, int nq,
-                                     int topk, int block_size, int max_blocks_per_seq, int num_blocks,
+                                     int nkv, int topk, int block_size, int max_blocks_per_seq, int num_blocks,
                                      float softmax_scale, int s2_tile, void* workspace_dev,
                                      size_t workspace_bytes, void* stream);
 
@@ -207,10 +226,10 @@ pa_status_t pa_fp8_mla_sparse_decode_kv_split(const void* q_nope_dev, const void
                                               const uint8_t* kn_quant_dev, const void* kr_dev,
                                               const float* kn_scales_dev, const int32_t* topk_dev,
                                               const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
-                                              void* out_dev, int B, int s1, int nq, int topk, int block_size,
-                                              int max_blocks_per_seq, int num_blocks, float softmax_scale,
-                                              int s2_tile, void* workspace_dev, size_t workspace_bytes,
-                                              void* stream);
+                                              void* out_dev, int B, int s1, int nq, int nkv, int topk,
+                                              int block_size, int max_blocks_per_seq, int num_blocks,
+                                              float softmax_scale, int s2_tile, void* workspace_dev,
+                                              size_t workspace_bytes, void* stream);
 
 /*
  * FP8 KV-cache writer, [P5] section 功能说明与计算公式: for every token i and
@@ -290,7 +309,11 @@ pa_status_t pa_fp8_kv_compress_epilog(uint8_t* cache_dev, const void* x_dev, con
                                       int round_scale, float x_scale, void* workspace_dev, size_t workspace_bytes,
                                       void* stream);
 
-/* Message of the last failed call on this host thread ("" if none). */
+/* Message of the last failed call on this host thread ("" if none); the
+ * pointer stays valid until the thread's next call into the library. */
+const char* pa_fp8_last_error_string(void);
+
+/* The same message (earlier name, kept for existing callers). */
 const char* pa_fp8_last_error(void);
 
 /* Library version string, e.g. "pa_fp8 0.1 gfx950". */

@@ -20,6 +20,16 @@ LIB = os.path.join(HERE, "liboracle.so")
 _lib = None
 
 
+def default_threads() -> int:
+    """Worker threads: the CPUs this process may run on, at most 16 (one GPU's
+    share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
     if force or not os.path.exists(LIB):
@@ -53,7 +63,7 @@ def lib():
         L.oracle_pa_fp8_decode_rows.argtypes = ([P] * 8 + [I] * 6 + [ctypes.c_double] + [I] * 4
                                                 + [P, I] + [P] * 4)
         L.oracle_pa_fp8_decode_rows.restype = I
-        L.oracle_mla_sparse_decode.argtypes = [P] * 6 + [I] * 7 + [ctypes.c_double] + [I] * 3 + [P] * 2
+        L.oracle_mla_sparse_decode.argtypes = [P] * 6 + [I] * 8 + [ctypes.c_double] + [I] * 3 + [P] * 2
         L.oracle_mla_sparse_decode.restype = I
         L.oracle_kv_compress_row_bytes.argtypes = [I, I]
         L.oracle_kv_compress_row_bytes.restype = I
@@ -137,7 +147,7 @@ def gqa_decode(inp, threads: int = None, b_range=None) -> dict:
     Ls = np.zeros((B * s1, nq), dtype=np.float64)
     rows = np.zeros((B, a["max_blocks"] * a["bs"]), dtype=np.int32)
     lo, hi = b_range if b_range is not None else (0, B)
-    threads = threads or min(os.cpu_count() or 1, max(1, hi - lo))
+    threads = threads or min(default_threads(), max(1, hi - lo))
 
     def run(rng):
         rc = L.oracle_pa_fp8_decode(
@@ -164,24 +174,26 @@ def gqa_decode_rows(inp, rows, threads: int = None) -> dict:
     out_bf = np.zeros((n, D), dtype=np.uint16)
     M = np.zeros(n)
     Ls = np.zeros(n)
-    threads = threads or min(os.cpu_count() or 1, max(1, n))
-    parts = np.array_split(np.arange(n), threads)
+    threads = threads or min(default_threads(), max(1, n))
+    # rows dealt round-robin in chunks of 8, so that threads share long and short sequences
+    parts = [np.concatenate([np.arange(c, min(c + 8, n)) for c in range(8 * t, n, 8 * threads)] or
+                            [np.zeros(0, dtype=np.int64)]) for t in range(threads)]
 
     def run(idx):
         if len(idx) == 0:
             return
-        i0, i1 = int(idx[0]), int(idx[-1]) + 1
-        sub = np.ascontiguousarray(rows[i0:i1])
-        o = np.zeros((i1 - i0, D)); ob = np.zeros((i1 - i0, D), dtype=np.uint16)
-        m = np.zeros(i1 - i0); l = np.zeros(i1 - i0)
+        k = len(idx)
+        sub = np.ascontiguousarray(rows[idx])
+        o = np.zeros((k, D)); ob = np.zeros((k, D), dtype=np.uint16)
+        m = np.zeros(k); l = np.zeros(k)
         rc = L.oracle_pa_fp8_decode_rows(
             _ptr(a["q"]), _ptr(a["q_scale"]), _ptr(a["k"]), _ptr(a["ks"]), _ptr(a["v"]), _ptr(a["vs"]),
             _ptr(a["table"]), _ptr(a["seqs"]), a["B"], a["s1"], a["nq"], a["nkv"], D, a["bs"], a["scale"],
-            a["s2_tile"], a["max_blocks"], a["num_blocks"], a["causal"], _ptr(sub), i1 - i0,
+            a["s2_tile"], a["max_blocks"], a["num_blocks"], a["causal"], _ptr(sub), k,
             _ptr(o), _ptr(ob), _ptr(m), _ptr(l))
         if rc != 0:
             raise ValueError(f"oracle_pa_fp8_decode_rows rc={rc}")
-        out[i0:i1] = o; out_bf[i0:i1] = ob; M[i0:i1] = m; Ls[i0:i1] = l
+        out[idx] = o; out_bf[idx] = ob; M[idx] = m; Ls[idx] = l
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(run, parts))
@@ -199,17 +211,18 @@ def mla_decode(inp, threads: int = None, b_range=None) -> dict:
     table = _np(inp["block_table"], np.int32)
     seqs = _np(inp["kv_act_seqs"], np.int32)
     B, s1, nq = cfg.B, cfg.s1, cfg.nq
-    K = topk.shape[1]
+    nkv = int(getattr(cfg, "nkv", 1))
+    K = topk.shape[1] // nkv
     s2_tile = int(inp.get("s2_tile", cfg.s2_tile))
     out = np.zeros((B * s1 * nq, 512), dtype=np.float64)
     out_bf = np.zeros((B * s1 * nq, 512), dtype=np.uint16)
     lo, hi = b_range if b_range is not None else (0, B)
-    threads = threads or min(os.cpu_count() or 1, max(1, hi - lo))
+    threads = threads or min(default_threads(), max(1, hi - lo))
 
     def run(rng):
         rc = L.oracle_mla_sparse_decode(
             _ptr(qn), _ptr(qr), _ptr(cache), _ptr(topk), _ptr(table), _ptr(seqs),
-            B, s1, nq, K, cfg.block_size, table.shape[1], cache.shape[0] // cfg.block_size,
+            B, s1, nq, nkv, K, cfg.block_size, table.shape[1], cache.shape[0] // cfg.block_size,
             float(inp["softmax_scale"]), s2_tile, rng[0], rng[1], _ptr(out), _ptr(out_bf))
         if rc != 0:
             raise ValueError(f"oracle_mla_sparse_decode rc={rc}")

@@ -96,6 +96,14 @@
  *        codes; its stored scale is bf16 0 (mode 0) or e8m0 code 0 (mode 1).
  *  R-ep-pad  bytes of a cache row past the written ones are left untouched.
  *  R-ep-slot slots < 0 or >= blockNum * blockSize are skipped.
+ *  R-mla-nkv [P2]'s signature gives topk_indices the shape (t, n_kv*topk) and
+ *        its loops run over KV heads, then the query group of each, while the
+ *        latent cache has one row per token slot: KV head h reads the shared
+ *        rows through its own slice [h*topk, (h+1)*topk), and query head hq
+ *        belongs to KV head hq / (nq / n_kv).
+ *  R-mla-pos a top-k position outside [0, seq) among the first n is clamped
+ *        into it (the table rule applied to positions; the page promises
+ *        in-range indices and says nothing of others).
  */
 #include <math.h>
 #include <stdint.h>
@@ -461,24 +469,30 @@ void oracle_mla_dequant_row(const uint8_t* row, double* kvec)
  * Decode batches [b_lo, b_hi) of the MLA-style sparse attention.
  *   q_nope [B*s1*nq, 512] bf16, q_rope [B*s1*nq, 64] bf16
  *   cache  [num_blocks*block_size, 672] bytes
- *   topk   [B*s1, topk] logical token ids (first n of each row used)
+ *   topk   [B*s1, nkv*topk] logical token ids: KV head h's slice is
+ *          [h*topk, (h+1)*topk) ([P2] API 签名: topk_indices (t, n_kv*topk));
+ *          the first n of each slice are used
  *   block_table [B, max_blocks], seqs [B]
  * Outputs: out_f64 [B*s1*nq, 512], out_bf16 (may be NULL).
  * Per query position s of batch b: n = clamp(seq - s1 + 1 + s, 0, topk).
+ * Query head hq belongs to KV head hq / (nq / nkv) ([P2] loops: KV head, then
+ * the query group of that head); every KV head reads the same latent rows,
+ * through its own top-k slice (reading R-mla-nkv).
  * Tiles of s2_tile index positions; P = exp(S - m_tile) cast to bf16 feeds
  * P.V, the unquantised P feeds the sum (readings stated in the header).
  */
 int oracle_mla_sparse_decode(const uint16_t* q_nope, const uint16_t* q_rope,
                              const uint8_t* cache, const int32_t* topk_idx,
                              const int32_t* block_table, const int32_t* seqs,
-                             int B, int s1, int nq, int topk, int block_size,
+                             int B, int s1, int nq, int nkv, int topk, int block_size,
                              int max_blocks, int num_blocks, double softmax_scale, int s2_tile,
                              int b_lo, int b_hi, double* out_f64, uint16_t* out_bf16)
 {
     const int DK = OR_MLA_NOPE + OR_MLA_ROPE, DV = OR_MLA_NOPE;
-    if (B <= 0 || s1 <= 0 || nq <= 0 || topk <= 0 || block_size <= 0 || max_blocks <= 0 ||
-        num_blocks <= 0 || s2_tile <= 0 || b_lo < 0 || b_hi > B || b_lo > b_hi)
+    if (B <= 0 || s1 <= 0 || nq <= 0 || nkv <= 0 || nq % nkv != 0 || topk <= 0 || block_size <= 0 ||
+        max_blocks <= 0 || num_blocks <= 0 || s2_tile <= 0 || b_lo < 0 || b_hi > B || b_lo > b_hi)
         return -1;
+    const int G = nq / nkv;
     double* K = malloc(sizeof(double) * (size_t)topk * DK);
     double* S = malloc(sizeof(double) * s2_tile);
     double* P = malloc(sizeof(double) * s2_tile);
@@ -495,18 +509,19 @@ int oracle_mla_sparse_decode(const uint16_t* q_nope, const uint16_t* q_rope,
             int n = seq - s1 + 1 + s;
             if (n < 0) n = 0;
             if (n > topk) n = topk;
-            const int32_t* idx = topk_idx + ((int64_t)b * s1 + s) * topk;
-            /* Gather + dequantise the n selected rows once per query token. */
+            for (int h = 0; h < nkv; ++h) {
+            const int32_t* idx = topk_idx + (((int64_t)b * s1 + s) * nkv + h) * topk;
+            /* Gather + dequantise the n selected rows once per (query token, KV head). */
             for (int j = 0; j < n; ++j) {
                 int p = idx[j];
-                if (p < 0) p = 0;                              /* defensive, as for the table */
+                if (p < 0) p = 0;                              /* R-mla-pos */
                 if (p >= seq) p = seq - 1;
                 int id = block_table[(int64_t)b * max_blocks + p / block_size];
                 if (id < 0 || id >= num_blocks) id = 0;
                 const uint8_t* row = cache + ((int64_t)id * block_size + p % block_size) * OR_MLA_ROW;
                 oracle_mla_dequant_row(row, K + (int64_t)j * DK);
             }
-            for (int hq = 0; hq < nq; ++hq) {
+            for (int hq = h * G; hq < (h + 1) * G; ++hq) {
                 const int64_t qrow = ((int64_t)b * s1 + s) * nq + hq;
                 for (int c = 0; c < OR_MLA_NOPE; ++c) qv[c] = oracle_bf16_decode(q_nope[qrow * OR_MLA_NOPE + c]);
                 for (int c = 0; c < OR_MLA_ROPE; ++c) qv[OR_MLA_NOPE + c] = oracle_bf16_decode(q_rope[qrow * OR_MLA_ROPE + c]);
@@ -541,6 +556,7 @@ int oracle_mla_sparse_decode(const uint16_t* q_nope, const uint16_t* q_rope,
                     out_f64[qrow * DV + c] = v;
                     if (out_bf16) out_bf16[qrow * DV + c] = oracle_bf16_encode(v);
                 }
+            }
             }
         }
     }

@@ -134,12 +134,14 @@ def mla_dequant_rows(cache_rows: np.ndarray) -> np.ndarray:
     return np.concatenate([kn, kr], axis=1)
 
 
-def mla_gather(inp, b, s):
+def mla_gather(inp, b, s, h=0):
+    """Dequantised K rows KV head h reads for query position s of batch b (its
+    top-k slice is columns [h*topk, h*topk + n) of the index row)."""
     cfg = inp["cfg"]
     bs = cfg.block_size
     seq = int(inp["kv_act_seqs"][b])
     n = max(0, min(seq - cfg.s1 + 1 + s, cfg.topk))
-    idx = inp["topk"][b * cfg.s1 + s, :n].cpu().numpy().astype(np.int64)
+    idx = inp["topk"][b * cfg.s1 + s, h * cfg.topk:h * cfg.topk + n].cpu().numpy().astype(np.int64)
     table = inp["block_table"][b].cpu().numpy().astype(np.int64)
     rows = table[idx // bs] * bs + idx % bs
     cache = inp["cache"].cpu().numpy()
@@ -148,7 +150,7 @@ def mla_gather(inp, b, s):
 
 def mla_closed_form_row(inp, b, s, hq, s2_tile):
     cfg = inp["cfg"]
-    K = mla_gather(inp, b, s)
+    K = mla_gather(inp, b, s, hq // (cfg.nq // cfg.nkv))
     r = (b * cfg.s1 + s) * cfg.nq + hq
     q = np.concatenate([inp["q_nope"][r].float().double().numpy(), inp["q_rope"][r].float().double().numpy()])
     n = K.shape[0]

@@ -61,7 +61,7 @@ def call(lib, **over):
 ])
 def test_host_validation_codes(lib, over, code):
     assert call(lib, **over) == code
-    assert len(lib.pa_fp8_last_error()) > 0
+    assert len(lib.pa_fp8_last_error_string()) > 0
 
 
 def test_workspace_query(lib):
@@ -98,7 +98,7 @@ def scatter(lib, **over):
 ])
 def test_scatter_host_validation_codes(lib, over, code):
     assert scatter(lib, **over) == code
-    assert len(lib.pa_fp8_last_error()) > 0
+    assert len(lib.pa_fp8_last_error_string()) > 0
 
 
 def epilog(lib, **over):
@@ -118,7 +118,7 @@ def epilog(lib, **over):
 ])
 def test_epilog_host_validation_codes(lib, over, code):
     assert epilog(lib, **over) == code
-    assert len(lib.pa_fp8_last_error()) > 0
+    assert len(lib.pa_fp8_last_error_string()) > 0
 
 
 def test_epilog_page_row_sizes_accepted(lib):
@@ -136,4 +136,32 @@ def test_causal_needs_the_whole_row_path(lib):
     """More than 32 query rows per KV head (s1=2, G=32) is outside the whole-row path."""
     rc = lib.pa_fp8_decode_causal(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 2, 128, 128,
                                   0.088, 256, 6, 8, FAKE, 1 << 20, None)
-    assert rc == 3 and b"whole-row" in lib.pa_fp8_last_error()
+    assert rc == 3 and b"whole-row" in lib.pa_fp8_last_error_string()
+
+
+def mla(lib, **over):
+    a = dict(qn=ALIGNED, qr=ALIGNED, cache=ALIGNED, topk=ALIGNED, table=ALIGNED, seqs=ALIGNED, out=ALIGNED,
+             B=2, s1=1, nq=64, nkv=2, K=512, bs=128, mbps=8, nb=16, scale=0.04, tile=512, ws=ALIGNED,
+             wsb=1 << 30, stream=None)
+    a.update(over)
+    return lib.pa_fp8_mla_sparse_decode(a["qn"], a["qr"], a["cache"], a["topk"], a["table"], a["seqs"], a["out"],
+                                        a["B"], a["s1"], a["nq"], a["nkv"], a["K"], a["bs"], a["mbps"], a["nb"],
+                                        a["scale"], a["tile"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(qn=None), 1), (dict(topk=None), 1), (dict(cache=None), 1),
+    (dict(B=0), 2), (dict(nkv=0), 2), (dict(nkv=3), 2), (dict(K=0), 2), (dict(scale=-1.0), 2),
+    (dict(nkv=4), 3), (dict(nq=48, nkv=1), 3), (dict(tile=1024), 3), (dict(bs=64), 3),
+    (dict(out=ctypes.c_void_p(0x10008)), 3), (dict(ws=None), 4), (dict(wsb=16), 4),
+])
+def test_mla_host_validation_codes(lib, over, code):
+    """nq / nkv query heads per KV head must come in blocks of 32 (nkv = 4 with
+    nq = 64 leaves 16); nkv must divide nq."""
+    assert mla(lib, **over) == code
+    assert len(lib.pa_fp8_last_error_string()) > 0
+
+
+def test_last_error_names_agree(lib):
+    assert call(lib, B=0) == 2
+    assert lib.pa_fp8_last_error_string() == lib.pa_fp8_last_error()

@@ -44,7 +44,7 @@ def test_config0_parity(B, oracle_mod):
     ref = oracle_mod.gqa_decode(inp)
     for ns in (0, 1, 2, 3):
         got = _run(B, inp, ns, "config0")
-        compare(got, ref["out_bf16"], f"config0 splits={ns}")
+        compare(got, ref, f"config0 splits={ns}")
 
 
 def test_config0_gather_and_q_codes_bit_exact(B, oracle_mod):
@@ -58,7 +58,7 @@ def test_config0_gather_and_q_codes_bit_exact(B, oracle_mod):
     torch.cuda.synchronize()
     assert np.array_equal(rows.cpu().numpy(), ref["rows"])
     assert np.array_equal(q8.cpu().numpy(), ref["q8"])
-    compare(gpu_out_float(out), ref["out_bf16"], "config0 debug")
+    compare(gpu_out_float(out), ref, "config0 debug")
 
 
 @pytest.mark.parametrize("num_splits", [0, 1])
@@ -109,7 +109,7 @@ def test_whole_row_most_pairs(B, oracle_mod, B_, nq, nkv):
                 max_blocks_per_seq=mb, s2_tile=256, seed=B_ + nkv)
     inp = synth.make_gqa_inputs(cfg)
     ref = oracle_mod.gqa_decode(inp)
-    compare(_run(B, inp, 0, "most pairs"), ref["out_bf16"], f"B={B_} nkv={nkv}")
+    compare(_run(B, inp, 0, "most pairs"), ref, f"B={B_} nkv={nkv}")
 
 
 @pytest.mark.parametrize("s2_tile", [128, 256, 512, 1024, 2048])
@@ -119,7 +119,7 @@ def test_tile_sizes(B, oracle_mod, s2_tile):
     inp = synth.make_gqa_inputs(cfg)
     ref = oracle_mod.gqa_decode(inp)
     for ns in (1, 0, 5):
-        compare(_run(B, inp, ns, f"tile{s2_tile}"), ref["out_bf16"], f"s2_tile={s2_tile} splits={ns}")
+        compare(_run(B, inp, ns, f"tile{s2_tile}"), ref, f"s2_tile={s2_tile} splits={ns}")
 
 
 @pytest.mark.parametrize("s1,nq,nkv", [(1, 12, 1), (1, 96, 8), (2, 48, 8), (4, 32, 4), (3, 48, 3),
@@ -131,7 +131,7 @@ def test_row_shapes(B, oracle_mod, s1, nq, nkv):
     inp = synth.make_gqa_inputs(cfg)
     ref = oracle_mod.gqa_decode(inp)
     for ns in (0, 1, 4):
-        compare(_run(B, inp, ns, "rows"), ref["out_bf16"], f"s1={s1} nq={nq} nkv={nkv} splits={ns}")
+        compare(_run(B, inp, ns, "rows"), ref, f"s1={s1} nq={nq} nkv={nkv} splits={ns}")
 
 
 def test_edge_lengths(B, oracle_mod):
@@ -142,7 +142,7 @@ def test_edge_lengths(B, oracle_mod):
     ref = oracle_mod.gqa_decode(inp)
     for ns in (1, 2, 3, 0):
         got = _run(B, inp, ns, "edges")
-        compare(got, ref["out_bf16"], f"edges splits={ns}")
+        compare(got, ref, f"edges splits={ns}")
         assert np.all(got.reshape(8, 8, 128)[0] == 0.0)
 
 
@@ -156,15 +156,19 @@ def test_clamped_length_and_bad_ids(B, oracle_mod):
     inp["block_table"] = t
     ref = oracle_mod.gqa_decode(inp)
     for ns in (1, 0):
-        compare(_run(B, inp, ns, "clamp"), ref["out_bf16"], f"clamp splits={ns}")
+        compare(_run(B, inp, ns, "clamp"), ref, f"clamp splits={ns}")
 
 
-def test_poison_beyond_sequence_bit_identical(B):
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_poison_beyond_sequence_bit_identical(B, num_splits):
+    """NaN codes and NaN scales in every token slot past the sequences and
+    random ids in unused table entries change no output bit, on the whole-row
+    path (0) and on the per-head path without and with splits."""
     cfg = _case("poison", B=4, seq_lens=(1, 200, 513, 1000), num_blocks=20, max_blocks_per_seq=8, seed=9)
-    clean = _run(B, synth.make_gqa_inputs(cfg), 0, "poison-clean")
+    clean = _run(B, synth.make_gqa_inputs(cfg), num_splits, "poison-clean")
     dirty_inp = synth.make_gqa_inputs(cfg, poison=True)
     assert torch.isnan(dirty_inp["k_scale"]).any()
-    dirty = _run(B, dirty_inp, 0, "poison-dirty")
+    dirty = _run(B, dirty_inp, num_splits, "poison-dirty")
     assert np.array_equal(clean, dirty)
 
 
@@ -199,24 +203,7 @@ def test_scaled_down_configs_full_parity(B, oracle_mod, cfg_id):
     inp = synth.make_gqa_inputs(cfg)
     ref = oracle_mod.gqa_decode(inp)
     for ns in (0, 1):
-        compare(_run(B, inp, ns, f"config{cfg_id}-small"), ref["out_bf16"], f"config{cfg_id} small splits={ns}")
-
-
-@pytest.mark.parametrize("cfg_id", [1, 2, 3])
-def test_full_size_configs_sampled_rows(B, oracle_mod, cfg_id):
-    """Full-size workloads in the benchmark's launch configuration; the oracle
-    recomputes a sample of output rows one by one."""
-    cfg = synth.CONFIGS[cfg_id]
-    print(f"[gpu] full-size config {cfg_id} generating on GPU", flush=True)
-    inp_d = synth.make_gqa_inputs(cfg, device="cuda")
-    out = _run_dev(B, inp_d, f"config{cfg_id}-full")
-    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp_d.items()}
-    nrows = cfg.B * cfg.s1 * cfg.nq
-    g = np.random.default_rng(cfg_id)
-    rows = np.unique(np.concatenate([[0, nrows - 1], g.choice(nrows, 46, replace=False)]))
-    ref = oracle_mod.gqa_decode_rows(host, rows)
-    got = out.reshape(nrows, cfg.D)[rows]
-    compare(got, ref["out_bf16"], f"config{cfg_id} full sampled rows")
+        compare(_run(B, inp, ns, f"config{cfg_id}-small"), ref, f"config{cfg_id} small splits={ns}")
 
 
 def _run_dev(B, inp_d, tag, num_splits=0):
@@ -241,7 +228,7 @@ def test_shared_workspace_between_paths(B, oracle_mod):
         print(f"[gpu] shared workspace call {i} splits={ns}", flush=True)
         out = B.decode_inputs(d, num_splits=ns, workspace=ws)
         torch.cuda.synchronize()
-        compare(gpu_out_float(out), ref["out_bf16"], f"shared workspace call {i} splits={ns}")
+        compare(gpu_out_float(out), ref, f"shared workspace call {i} splits={ns}")
 
 
 @pytest.mark.parametrize("s1,nq,nkv,s2_tile,seqs", [
@@ -257,20 +244,6 @@ def test_causal_parity(B, oracle_mod, s1, nq, nkv, s2_tile, seqs):
     inp = dict(synth.make_gqa_inputs(cfg), causal=True)
     ref = oracle_mod.gqa_decode(inp)
     got = _run(B, inp, 0, "causal")
-    compare(got, ref["out_bf16"], f"causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile}")
+    compare(got, ref, f"causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile}")
     if s1 == 1:
         assert np.array_equal(got, _run(B, dict(inp, causal=False), 0, "plain"))
-
-
-def test_causal_full_size_config3_sampled_rows(B, oracle_mod):
-    """The multi-token workload (B=256, s1=4, nq=32, nkv=4) decoded causally."""
-    cfg = synth.CONFIGS[3]
-    print("[gpu] causal config 3 generating on GPU", flush=True)
-    inp_d = dict(synth.make_gqa_inputs(cfg, device="cuda"), causal=True)
-    out = _run_dev(B, inp_d, "config3-causal")
-    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp_d.items()}
-    nrows = cfg.B * cfg.s1 * cfg.nq
-    g = np.random.default_rng(33)
-    rows = np.unique(np.concatenate([[0, nrows - 1], g.choice(nrows, 62, replace=False)]))
-    ref = oracle_mod.gqa_decode_rows(host, rows)
-    compare(out.reshape(nrows, cfg.D)[rows], ref["out_bf16"], "config3 causal sampled rows")

@@ -119,7 +119,7 @@ def test_writer_then_decode(B, oracle_mod):
     out_direct = gpu_out_float(B.decode_inputs(d))
     torch.cuda.synchronize()
     assert np.array_equal(out_rebuilt, out_direct)
-    compare(out_rebuilt, oracle_mod.gqa_decode(inp)["out_bf16"], "writer then decode")
+    compare(out_rebuilt, oracle_mod.gqa_decode(inp), "writer then decode")
 
 
 def test_writer_full_size_prefill(B, oracle_mod):

@@ -410,6 +410,23 @@ def test_mla_closed_form(oracle_mod, s2_tile):
             np.testing.assert_allclose(res["out"][b * cfg.nq + hq], ref, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("nkv", [2, 3])
+def test_mla_kv_heads_read_their_own_slice(oracle_mod, nkv):
+    """nkv KV heads: query head hq uses the top-k slice of KV head hq / (nq / nkv)
+    (the page's topk_indices (t, n_kv*topk)); the closed form gathers that
+    slice itself.  A dropped slice offset or a wrong head-to-slice mapping
+    fails here, since the slices are drawn independently."""
+    cfg = mla_small(nq=2 * nkv, nkv=nkv, s1=2, seq_lens=(200, 40), topk=64, seed=40 + nkv)
+    inp = synth.make_mla_inputs(cfg)
+    assert not np.array_equal(inp["topk"][:, :64].numpy(), inp["topk"][:, 64:128].numpy())
+    res = oracle_mod.mla_decode(inp)
+    for b in range(cfg.B):
+        for s in range(cfg.s1):
+            for hq in range(cfg.nq):
+                ref = cf.mla_closed_form_row(inp, b, s, hq, cfg.s2_tile)
+                np.testing.assert_allclose(res["out"][(b * cfg.s1 + s) * cfg.nq + hq], ref, rtol=1e-12, atol=1e-14)
+
+
 def test_mla_valid_count_formula(oracle_mod):
     for seq, s1, s, topk, n in GOLDEN["mla_valid_count"]["cases"]:
         assert max(0, min(seq - s1 + 1 + s, topk)) == n
