@@ -95,23 +95,26 @@ bool use_rows_path(int B, int s1, int nq, int nkv, int s2_tile, int num_splits) 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct WorkspaceLayout {
-    size_t meta, part_ml, part_o, total;   // meta: arrival counters (per-head path) or the partition (whole-row path)
+    size_t meta, tags, part_ml, part_o, total;   // meta: arrival counters (per-head path) or the partition
 };
 
 // Per-head path with splits: [B*nkv int32 counters | pad][B*nkv*nsplit*R*2 | pad][B*nkv*nsplit*R*128]
 // Whole-row path:             [B*nkv int32, untouched | pad][B*nkv+2 int32 partition | pad]
-//                             [B*nkv*KMAX*R*2 | pad][B*nkv*KMAX*R*128]
-// with KMAX = tiles per sequence at full capacity (a (batch, head) is split at most that often).
+//                             [256*2 int32 slot tags | pad][256*2*HG*R*2 | pad][256*2*HG*R*128]
+// with two partial slots per workgroup (its first and last segment, the only ones that can
+// be split), HG KV heads per workgroup and R query rows per KV head padded to 16.
 // The whole-row path never writes the first B*nkv words, so the per-head path's arrival
 // counters stay zero when one workspace serves calls of both paths.
-WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit, bool rows, int kmax) {
-    WorkspaceLayout l = {0, 0, 0, 0};
+WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit, bool rows) {
+    WorkspaceLayout l = {0, 0, 0, 0, 0};
     if (rows) {
         const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
+        const size_t slots = (size_t)pa::kRowsMaxGrid * 2 * pa::rows_group(nkv);
         l.meta = align256(units * sizeof(int32_t));
-        l.part_ml = l.meta + align256(((size_t)B * nkv + 2) * sizeof(int32_t));
-        l.part_o = l.part_ml + align256(units * kmax * R * 2 * sizeof(float));
-        l.total = l.part_o + units * kmax * R * pa::kHeadDim * sizeof(float);
+        l.tags = l.meta + align256(((size_t)B * nkv + 2) * sizeof(int32_t));
+        l.part_ml = l.tags + align256((size_t)pa::kRowsMaxGrid * 2 * sizeof(int32_t));
+        l.part_o = l.part_ml + align256(slots * R * 2 * sizeof(float));
+        l.total = l.part_o + slots * R * pa::kHeadDim * sizeof(float);
         return l;
     }
     if (nsplit <= 1) return l;
@@ -148,7 +151,7 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
                     "at most 32 query rows per KV head, s2_tile 128-1024");
     const int nsplit = rows ? 1 : plan_splits(B, nkv, max_tiles, num_splits);
     const int tps = (max_tiles + nsplit - 1) / nsplit;
-    const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit, rows, max_tiles);
+    const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit, rows);
     const size_t need = lay.total;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)", need, nsplit,
@@ -170,14 +173,15 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.out = static_cast<uint16_t*>(out);
     if (need > 0) {
         char* base = static_cast<char*>(workspace);
-        if (rows)
+        if (rows) {
             p.rows_meta = reinterpret_cast<int32_t*>(base + lay.meta);
-        else
+            p.part_tag = reinterpret_cast<int32_t*>(base + lay.tags);
+        } else {
             p.counters = reinterpret_cast<int32_t*>(base + lay.meta);
+        }
         p.part_ml = reinterpret_cast<float*>(base + lay.part_ml);
         p.part_o = reinterpret_cast<float*>(base + lay.part_o);
     }
-    p.rows_kmax = max_tiles;
     p.dbg_rows = debug ? rows_dev : nullptr;
     p.dbg_q8 = debug ? q8_dev : nullptr;
     p.B = B;
@@ -295,7 +299,7 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
     const bool rows = use_rows_path(B, s1, nq, nkv, s2_tile, num_splits);
     const int nsplit = rows ? 1 : plan_splits(B, nkv, max_tiles, num_splits);
-    *bytes_host = layout_for(B, s1, nq, nkv, nsplit, rows, max_tiles).total;
+    *bytes_host = layout_for(B, s1, nq, nkv, nsplit, rows).total;
     if (splits_host) *splits_host = nsplit;
     return PA_OK;
 }

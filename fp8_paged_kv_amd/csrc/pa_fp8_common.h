@@ -22,14 +22,15 @@ struct DecodeParams {
     uint16_t* out;              // [B*s1, nq, 128] bf16
     int32_t* counters;          // per-head path: [B*nkv] arrival counters (zero between calls)
     int32_t* rows_meta;         // whole-row path: cost prefix over (batch, head group), workgroups used
-    float* part_o;              // [B*nkv, nsplit, rows_pad, 128]
-    float* part_ml;             // [B*nkv, nsplit, rows_pad, 2]  (M in log2 units, L)
+    int32_t* part_tag;          // whole-row path: [256, 2] (batch, head group) of each partial slot, -1 = none
+    float* part_o;              // per-head path: [B*nkv, nsplit, rows_pad, 128];
+                                // whole-row path: [256, 2, HG, rows_pad, 128] (workgroup, first / last segment)
+    float* part_ml;             // the same with 2 floats per row (M in log2 units, L)
     int32_t* dbg_rows;          // [B, capacity] or null
     uint8_t* dbg_q8;            // [B*s1, nq, 128] or null
     int B, s1, nq, nkv, G, rows;
     int s2_tile, max_blocks, num_blocks, capacity;
     int nsplit, nsplit_pad, tiles_per_split;
-    int rows_kmax;              // whole-row path: partial slots per (batch, KV head) = tiles
     int causal;                 // whole-row path: position s of s1 sees the first seq - s1 + 1 + s tokens
     float softmax_scale;
 };
@@ -82,6 +83,8 @@ bool mla_supported(int nq, int nkv, int s2_tile);
 hipError_t launch_mla(const MlaParams& p, hipStream_t stream);
 int grid_size(const DecodeParams& p);
 bool rows_path_supported(int nkv, int s2_tile, int rows, int s1, int nq, int B);
+constexpr int kRowsMaxGrid = 256;   // whole-row path: at most one workgroup per CU, at most 256
+int rows_group(int nkv);            // KV heads per whole-row workgroup
 hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t stream, bool debug);
 hipError_t launch_fill_rows(const DecodeParams& p, hipStream_t stream);
 

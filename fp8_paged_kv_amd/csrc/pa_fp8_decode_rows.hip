@@ -296,15 +296,22 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                     h0 = 0;
                     ++b;
                 }
-                if (v >= BV) return;
+                if (v >= BV) {
+                    if (threadIdx.x == 0) a.part_tag[2 * g] = a.part_tag[2 * g + 1] = -1;
+                    return;
+                }
                 seq = lds_uniform(&s_seq[b]);
             }
             pv = lds_uniform(&s_pref[v]);
             mid = pv + kSegW / 2 + min(NBLK, nblocks(seq));
         }
-        if (mid >= hi) return;                      // no midpoint in this range: no work
+        if (mid >= hi) {                            // no midpoint in this range: no work
+            if (threadIdx.x == 0) a.part_tag[2 * g] = a.part_tag[2 * g + 1] = -1;
+            return;
+        }
         cur = make_unit(v, b, h0, seq, t, true);   // its table loads overlap the Q staging below
     }
+    const int first_v = cur.v;               // the range's first (batch, group)
     Unit nxt;
     bool nxt_ready = false;                  // finish_ids(nxt) done
 
@@ -399,7 +406,6 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     int mlim = 0;                            // the smallest of them over the rows
     float M_s[NRB], L_s[NRB], M_o[NRB][4];
     f32x4 O[NRB][8];
-    int seg_t0 = 0;                          // first tile of the current segment
 
     // prologue: Q of the first sequence, then the first AHEAD steps (a unit has >= 2)
     issue_q(cur.b, cur.h0, 0);
@@ -444,7 +450,6 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         const bool seg_start = cur.v != prev_v;
         if (seg_start) {
             vs_buf ^= 1;
-            seg_t0 = cur.t;
         }
         const int h = cur.h0 + hl;
         float sv[NRB][NQ][8];
@@ -675,6 +680,15 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         if (seg_end) {
             // finished here unless some tile of the sequence lies outside this range
             const bool split = unit_mid(cur, 0) < lo || unit_mid(cur, (cur.seq + T - 1) / T - 1) >= hi;
+            // only a range's first and last segments can be split: a split first segment
+            // leaves its partial in slot (g, 0), a split last one in (g, 1); the tags name
+            // the (batch, group) of each slot (-1: none), written once per call
+            const bool first_seg = cur.v == first_v, last_seg = nxt.nvs == 0;
+            const int64_t slot_base = (int64_t)(2 * g + (first_seg ? 0 : 1)) * HG + hl;
+            if (threadIdx.x == 0) {
+                if (first_seg) a.part_tag[2 * g] = split ? cur.v : -1;
+                if (last_seg) a.part_tag[2 * g + 1] = (split && !first_seg) ? cur.v : -1;
+            }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 // the two halves of each head: wave p = 1 hands its O and L to wave p = 0
@@ -726,7 +740,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                             *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + 8 * lr) =
                                 i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
                         } else {
-                            const int64_t slot = ((int64_t)cur.b * nkv + h) * a.rows_kmax + seg_t0;
+                            const int64_t slot = slot_base;
                             float* po = a.part_o + (slot * R + rr) * kHeadDim + 8 * lr;
                             *reinterpret_cast<f32x4*>(po) = f32x4{O[rb][0][i], O[rb][1][i], O[rb][2][i], O[rb][3][i]};
                             *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[rb][4][i], O[rb][5][i], O[rb][6][i], O[rb][7][i]};
@@ -759,13 +773,14 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 // threads per query row (8 columns each).  The partition is recomputed from what
 // the decode kernel published (cost prefix and workgroup count): decode
 // workgroup g owns the tiles whose cost midpoints lie in [g C / Geff,
-// (g + 1) C / Geff) and wrote its partial into the slot of its first tile.
+// (g + 1) C / Geff), so the pair's tiles lie in the ranges of the owners g0..g1 of
+// its first and last tiles, each holding one segment of it; the slot tags say
+// which of a workgroup's two slots holds that segment.
 template <int NBLK, int HG>
 __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) {
-    __shared__ int s_tf[257];
     const int NG = a.nkv / HG, BV = a.B * NG;
     const int bh = blockIdx.x, b = bh / a.nkv, h = bh - b * a.nkv;
-    const int v = b * NG + h / HG;
+    const int v = b * NG + h / HG, hl = h - (h / HG) * HG;
     const int* meta = a.rows_meta;
     // independent loads first
     const int64_t C = meta[BV];
@@ -786,40 +801,28 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
     };
     auto owner = [&](int64_t x) -> int { return floor_div64((x + 1) * Geff - 1, C); };
     const int g0 = owner(mid_of(0)), g1 = owner(mid_of(nt - 1));
-    if (g0 == g1) return;                      // finished in place by the decode kernel
+    if (g0 == g1 || rr >= a.rows) return;      // finished in place by the decode kernel
     const int n = g1 - g0 + 1;                 // <= the decode grid (<= 256)
-    for (int i = threadIdx.x; i <= n; i += blockDim.x) {
-        int tf = nt;
-        if (i == 0) {
-            tf = 0;
-        } else if (i < n) {
-            // first tile whose midpoint is >= the start of workgroup g0 + i's range
-            const int64_t x = floor_div64((int64_t)(g0 + i) * C, Geff);
-            const int64_t d = x - pv - kSegW - NBLK;
-            int t = d <= 0 ? 0 : (int)min((int64_t)nt, (d + 2 * NBLK - 1) / (2 * NBLK));
-            while (t > 0 && mid_of(t - 1) >= x) --t;
-            while (t < nt && mid_of(t) < x) ++t;
-            tf = t;
-        }
-        s_tf[i] = tf;
-    }
-    __syncthreads();
-    if (rr >= a.rows) return;
-    const int64_t base = ((int64_t)b * a.nkv + h) * a.rows_kmax;
     float Mx = -INFINITY, L = 0.f;
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
     constexpr int SB = 4;                      // segments whose loads are issued together
     for (int i0 = 0; i0 < n; i0 += SB) {
+        int k[SB];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int g = min(g0 + i0 + j, g1);
+            const int t0 = a.part_tag[2 * g], t1 = a.part_tag[2 * g + 1];
+            k[j] = (i0 + j >= n) ? -1 : (t0 == v ? 0 : (t1 == v ? 1 : -1));
+        }
         float m[SB], l[SB];
         f32x4 x0[SB], x1[SB];
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-            const int i = i0 + j;
-            const bool ok = i < n && s_tf[i] < s_tf[i + 1];
-            const int64_t slot = base + (ok ? s_tf[i] : 0);
-            const float* pm = a.part_ml + (slot * R + rr) * 2;
-            const float* po = a.part_o + (slot * R + rr) * kHeadDim + d0;
-            m[j] = ok ? pm[0] : -INFINITY;
+            const int g = min(g0 + i0 + j, g1);
+            const int64_t slot = ((int64_t)(2 * g + (k[j] > 0 ? 1 : 0)) * HG + hl) * R + rr;
+            const float* pm = a.part_ml + slot * 2;
+            const float* po = a.part_o + slot * kHeadDim + d0;
+            m[j] = k[j] >= 0 ? pm[0] : -INFINITY;
             l[j] = pm[1];
             x0[j] = *reinterpret_cast<const f32x4*>(po);
             x1[j] = *reinterpret_cast<const f32x4*>(po + 4);
@@ -827,7 +830,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
             if (m[j] == -INFINITY) continue;
-            // running merge in segment order: rescale to the larger maximum
+            // running merge in range order: rescale to the larger maximum
             const float mn = fmaxf(Mx, m[j]);
             const float fa = __builtin_amdgcn_exp2f(Mx - mn), fb = __builtin_amdgcn_exp2f(m[j] - mn);
             L = L * fa + l[j] * fb;
@@ -891,7 +894,7 @@ hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t st, bo
     // one workgroup per CU (163 KB of LDS with two heads, 87 KB with one): the ranges
     // have equal cost, so every workgroup must be resident at once
     // (at most 256: the merge kernel's table of one sequence's workgroups holds 256)
-    const int grid = cus < 256 ? cus : 256;
+    const int grid = cus < kRowsMaxGrid ? cus : kRowsMaxGrid;
     if (rows_group(p.nkv) == 2) return launch_rows_hg<2>(p, grid, st, dbg);
     return launch_rows_hg<1>(p, grid, st, dbg);
 }
