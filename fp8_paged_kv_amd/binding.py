@@ -18,7 +18,8 @@ LIB_PATH = os.environ.get("PA_FP8_LIB") or os.path.join(PKG, "libpa_fp8.so")
 
 PA_OK, PA_ERR_NULLPTR, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
 
-EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_debug", "pa_fp8_decode_causal",
+EXPORTS = ("pa_fp8_decode_workspace_size", "pa_fp8_decode", "pa_fp8_decode_noalloc", "pa_fp8_decode_debug",
+           "pa_fp8_decode_causal",
            "pa_fp8_mla_workspace_size", "pa_fp8_mla_sparse_decode",
            "pa_fp8_mla_sparse_decode_kv_split", "pa_fp8_scatter_kv_cache",
            "pa_fp8_kv_compress_epilog_workspace_size", "pa_fp8_kv_compress_epilog",
@@ -47,6 +48,8 @@ def lib():
         gqa = [P] * 9 + [I] * 6 + [F] + [I] * 4 + [P, Z]
         L.pa_fp8_decode.argtypes = gqa + [P]
         L.pa_fp8_decode.restype = I
+        L.pa_fp8_decode_noalloc.argtypes = [P] * 9 + [I] * 6 + [F] + [I] * 4 + [P]
+        L.pa_fp8_decode_noalloc.restype = I
         L.pa_fp8_decode_causal.argtypes = [P] * 9 + [I] * 6 + [F] + [I] * 3 + [P, Z, P]
         L.pa_fp8_decode_causal.restype = I
         L.pa_fp8_decode_debug.argtypes = gqa + [P, P, P]
@@ -147,6 +150,30 @@ def decode(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_s
         _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),
         int(s2_tile), mbps, nblk, int(num_splits), _ptr(workspace), wbytes, _stream(stream)))
     return out
+
+
+def decode_noalloc(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_seqs, softmax_scale,
+                   s2_tile, num_splits=0, out=None, stream=None, s1=None):
+    """pa_fp8_decode_noalloc: the decode with the library's own scratch instead of a
+    workspace (allocates nothing when ``out`` is given)."""
+    B, s1, nq, nkv, D, bs, nblk, mbps = _shapes(q, k_cache, block_table, kv_act_seqs, s1)
+    _checked_inputs(dict(q=q, q_scale=q_scale, k_cache=k_cache, k_scale=k_scale, v_cache=v_cache,
+                         v_scale=v_scale, block_table=block_table, kv_act_seqs=kv_act_seqs, out=out))
+    if out is None:
+        out = torch.empty((B * s1, nq, D), dtype=torch.bfloat16, device=q.device)
+    _check(lib().pa_fp8_decode_noalloc(
+        _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+        _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),
+        int(s2_tile), mbps, nblk, int(num_splits), _stream(stream)))
+    return out
+
+
+def decode_noalloc_inputs(inp: dict, num_splits=0, out=None, stream=None):
+    """decode_noalloc() on a dict produced by fp8_paged_kv_amd.synth.make_gqa_inputs."""
+    return decode_noalloc(inp["q"], inp["q_scale"], inp["k_cache"], inp["k_scale"], inp["v_cache"], inp["v_scale"],
+                          inp["block_table"], inp["kv_act_seqs"], inp["softmax_scale"],
+                          inp.get("s2_tile", inp["cfg"].s2_tile), num_splits=num_splits, out=out, stream=stream,
+                          s1=inp["cfg"].s1)
 
 
 def decode_debug(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_seqs, softmax_scale,

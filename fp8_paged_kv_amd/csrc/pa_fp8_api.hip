@@ -7,9 +7,16 @@
 #include <cstdio>
 #include <cstring>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/pa_fp8.h"
 #include "pa_fp8_common.h"
+
+// Device memory that pa_fp8_decode_noalloc uses in place of a caller's
+// workspace: one array per device, held from the library's load until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[PA_FP8_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -94,6 +101,35 @@ bool use_rows_path(int B, int s1, int nq, int nkv, int s2_tile, int num_splits) 
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Zero n int32 words (the per-head path's arrival counters in the scratch array).
+__global__ void zero_words_kernel(int32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current.
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];
+
+pa_status_t scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(PA_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return PA_OK;
+}
+
 struct WorkspaceLayout {
     size_t meta, tags, part_ml, part_o, total;   // meta: arrival counters (per-head path) or the partition
 };
@@ -131,7 +167,7 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
                 const int32_t* seqs, void* out, int B, int s1, int nq, int nkv, int D, int block_size,
                 float softmax_scale, int s2_tile, int max_blocks, int num_blocks, int num_splits,
                 void* workspace, size_t workspace_bytes, int32_t* rows_dev, uint8_t* q8_dev,
-                bool debug, bool causal, void* stream) {
+                bool debug, bool causal, void* stream, bool clear_counters = false) {
     g_err[0] = 0;
     if (!q || !q_scale || !k_cache || !k_scale || !v_cache || !v_scale || !block_table || !seqs || !out)
         return fail(PA_ERR_NULLPTR, "a required tensor pointer is NULL");
@@ -201,6 +237,14 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.causal = causal ? 1 : 0;
 
     hipError_t e;
+    if (clear_counters && p.counters) {
+        // a workspace the caller did not zero (the library's scratch): clear the arrival counters
+        const int n = B * nkv;
+        hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           p.counters, n);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    }
     if (rows) {
         if (debug && p.dbg_rows) {
             e = pa::launch_fill_rows(p, static_cast<hipStream_t>(stream));
@@ -314,6 +358,34 @@ pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev, const uin
                kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
                max_blocks_per_seq, num_blocks, num_splits, workspace_dev, workspace_bytes, nullptr, nullptr,
                false, false, stream);
+}
+
+pa_status_t pa_fp8_decode_noalloc(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
+                                  const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,
+                                  const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev, void* out_dev,
+                                  int B, int s1, int nq, int nkv, int D, int block_size, float softmax_scale,
+                                  int s2_tile, int max_blocks_per_seq, int num_blocks, int num_splits,
+                                  void* stream) {
+    g_err[0] = 0;
+    if (!q_dev || !q_scale_dev || !k_cache_dev || !k_scale_dev || !v_cache_dev || !v_scale_dev ||
+        !block_table_dev || !kv_act_seqs_dev || !out_dev)
+        return fail(PA_ERR_NULLPTR, "a required tensor pointer is NULL");
+    size_t need = 0;
+    int nsplit = 0;
+    pa_status_t st = pa_fp8_decode_workspace_size(B, s1, nq, nkv, D, block_size, max_blocks_per_seq, s2_tile,
+                                                  num_splits, &need, &nsplit);
+    if (st != PA_OK) return st;
+    if (need > (size_t)PA_FP8_NOALLOC_SCRATCH_BYTES)
+        return fail(PA_ERR_WORKSPACE, "this call needs %zu bytes of scratch (%d splits); the library holds %zu "
+                    "per device: use pa_fp8_decode with a workspace", need, nsplit,
+                    (size_t)PA_FP8_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != PA_OK) return st;
+    return run(q_dev, q_scale_dev, k_cache_dev, k_scale_dev, v_cache_dev, v_scale_dev, block_table_dev,
+               kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
+               max_blocks_per_seq, num_blocks, num_splits, ws, (size_t)PA_FP8_NOALLOC_SCRATCH_BYTES, nullptr,
+               nullptr, false, false, stream, true);
 }
 
 pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,

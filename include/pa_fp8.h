@@ -134,6 +134,32 @@ pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev,
                           void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * pa_fp8_decode without a workspace argument.  The partial results of split
+ * sequences live in a static scratch array of the library,
+ * PA_FP8_NOALLOC_SCRATCH_BYTES per device, held from the library's load
+ * until the process ends; this call allocates and frees nothing.  A call
+ * whose workspace (pa_fp8_decode_workspace_size, same arguments) exceeds
+ * that size returns PA_ERR_WORKSPACE before anything is launched (the
+ * whole-row path needs at most about 17 MB; the per-head path grows with
+ * B * nkv * splits).  Every call on one device shares that device's array,
+ * which keeps the last call's contents: calls that overlap in time on one
+ * GPU (other streams, other host threads) race and give wrong results.
+ * Same arguments (minus the workspace), rules, results and other status
+ * codes as pa_fp8_decode.
+ */
+#define PA_FP8_NOALLOC_SCRATCH_BYTES (32u << 20)
+pa_status_t pa_fp8_decode_noalloc(const void* q_dev, const float* q_scale_dev,
+                                  const uint8_t* k_cache_dev, const float* k_scale_dev,
+                                  const uint8_t* v_cache_dev, const float* v_scale_dev,
+                                  const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev,
+                                  void* out_dev,
+                                  int B, int s1, int nq, int nkv, int D, int block_size,
+                                  float softmax_scale, int s2_tile, int max_blocks_per_seq, int num_blocks,
+                                  int num_splits, void* stream);
+
+/*
  * pa_fp8_decode plus two dumps taken from inside the kernel:
  *   rows_dev [B, max_blocks_per_seq * block_size] int32: for every logical
  *            token p < seq_b the physical token row (block_id * block_size +

@@ -165,3 +165,27 @@ def test_mla_host_validation_codes(lib, over, code):
 def test_last_error_names_agree(lib):
     assert call(lib, B=0) == 2
     assert lib.pa_fp8_last_error_string() == lib.pa_fp8_last_error()
+
+
+def noalloc(lib, **over):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, v=FAKE, vs=FAKE, table=FAKE, seqs=FAKE, out=FAKE,
+             B=2, s1=1, nq=8, nkv=2, D=128, bs=128, scale=0.088, tile=256, mbps=6, nblocks=8, splits=1, stream=None)
+    a.update(over)
+    return lib.pa_fp8_decode_noalloc(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["table"], a["seqs"],
+                                     a["out"], a["B"], a["s1"], a["nq"], a["nkv"], a["D"], a["bs"], a["scale"],
+                                     a["tile"], a["mbps"], a["nblocks"], a["splits"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(seqs=None), 1), (dict(B=0), 2), (dict(nq=7), 2), (dict(D=64), 3),
+    # per-head path with 64 splits of 64 rows for 64 sequences: about 136 MB of partials
+    (dict(B=64, nq=64, nkv=1, mbps=1024, splits=64), 4),
+])
+def test_noalloc_host_validation_codes(lib, over, code):
+    """The no-allocation entry point rejects bad arguments, and a call whose
+    workspace exceeds the library's scratch, before touching the device."""
+    assert noalloc(lib, **over) == code
+    msg = lib.pa_fp8_last_error_string()
+    assert len(msg) > 0
+    if code == 4:
+        assert b"scratch" in msg
