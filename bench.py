@@ -41,9 +41,14 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
-    ap.add_argument("--op", choices=["decode", "scatter", "epilog"], default="decode",
+    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling"], default="decode",
                     help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
-                         "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows")
+                         "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows; "
+                         "ceiling: read-only probes of config 1's paged access pattern and of a contiguous "
+                         "buffer, beside the decode")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="headline only: skip the other workloads' entries")
+    ap.add_argument("--secondary-steps", type=int, default=50)
     ap.add_argument("--splits", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--causal", action="store_true",
                     help="GQA: causal multi-token decode (position s of s1 sees the first seq - s1 + 1 + s tokens)")
@@ -106,12 +111,11 @@ def time_calls(binding, sets, steps, warmup, splits, out, ws):
     return _timed(call, steps, warmup)
 
 
-def cpu_baseline(cfg, sets, seqs, target_s):
-    """The oracle as it stands, on the first sequences of the same workload."""
-    import numpy as np
+def cpu_baseline(cfg, host, seqs, target_s):
+    """The oracle as it stands, on the first sequences of the same workload
+    (``host``: the first timed input set, copied to the host)."""
     from fp8_paged_kv_amd import synth
     from oracle import oracle
-    host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in sets[0].items()}
     try:
         threads = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -176,6 +180,8 @@ def main():
         return run_scatter(args)
     if args.op == "epilog":
         return run_epilog(args)
+    if args.op == "ceiling":
+        return run_ceiling(args)
     if args.config == 4:
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
@@ -218,6 +224,7 @@ def main():
                               "wall_us_per_call": round(wall / args.steps * 1e6, 2)}), flush=True)
         return
 
+    host0 = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in sets[0].items()}
     wall, region, ev, nsplit = run(args.splits, args.steps, args.warmup, sets)
     ms_per_step = wall / args.steps * 1e3
     mean_ev = sum(ev) / len(ev)
@@ -274,55 +281,188 @@ def main():
         "unit": "TFLOP/s", "frac": round(flops / (region * 1e-3) / 1e12 / 2500.0, 4),
         "note": "analytic, exact lengths; the work executed with query rows padded to 16 is counted by "
                 "SQ_INSTS_VALU_MFMA_MOPS_BF16 in profiles/mfma_counters_glm45_b32_and_mla.md"}
+    if not args.no_secondary and args.config == 1 and not args.causal and args.splits == 0:
+        del sets
+        torch.cuda.empty_cache()
+        line["secondary"] = secondary_entries(args)
+        sets = None
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, sets, seqs, args.cpu_target_s)
+        line["cpu_baseline"] = cpu_baseline(cfg, host0, seqs, args.cpu_target_s)
     print(json.dumps(line), flush=True)
 
 
-def run_mla(args):
-    """The MLA-style sparse decode workload (B=16, nq=128, topk 2048, seq 4k-32k)."""
+def measure_gqa(cfg_id, causal, steps, warmup, rotate):
+    """Event-timed decode calls on one GQA workload (rotating input sets):
+    algorithmic bytes, us per call and the HBM roofline fraction."""
+    import torch
+    from fp8_paged_kv_amd import binding, synth
+    cfg = synth.CONFIGS[cfg_id]
+    sets, seqs = make_sets(cfg, rotate)
+    for st in sets:
+        st["causal"] = causal
+    nbytes = synth.gqa_algorithmic_bytes(cfg, seqs)
+    out = torch.empty((cfg.B * cfg.s1, cfg.nq, cfg.D), dtype=torch.bfloat16, device="cuda")
+    need, _ = binding.workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.nkv, cfg.D, cfg.block_size, cfg.max_blocks_per_seq,
+                                     cfg.s2_tile, 0)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    _, region, ev = time_calls(binding, sets, steps, warmup, 0, out, ws)
+    del sets
+    torch.cuda.empty_cache()
+    gbs = nbytes / (region * 1e-3) / 1e9
+    return {"workload": cfg.name + ("-causal" if causal else ""), "algorithmic_bytes_per_call": nbytes,
+            "us_per_call": round(region * 1e3, 2), "median_us": round(ev[len(ev) // 2] * 1e3, 2),
+            "calls_per_s": round(1e3 / region, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "kernel": "pa::decode_rows_kernel + pa::merge_rows_kernel"}
+
+
+def measure_mla(kv_split, steps, warmup, rotate):
+    """Event-timed MLA sparse decode calls: bf16 MFMA roofline (and HBM beside it)."""
     import torch
     from fp8_paged_kv_amd import binding, synth
     cfg = synth.CONFIGS[4]
     first = synth.make_mla_inputs(cfg, device="cuda")
     seqs = first["kv_act_seqs"].cpu().tolist()
     sets = [first] + [synth.make_mla_inputs(cfg, device="cuda", seed=1000 + 17 * i + cfg.seed, seq_lens=seqs)
-                      for i in range(1, max(1, args.rotate))]
+                      for i in range(1, max(1, rotate))]
+    if kv_split:
+        sets = [synth.mla_kv_split(st) for st in sets]
+    run_one = binding.mla_decode_kv_split_inputs if kv_split else binding.mla_decode_inputs
     out = torch.empty((cfg.B * cfg.s1 * cfg.nq, 512), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(binding.mla_workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
                      device="cuda")
-    if args.kv_split:
-        sets = [synth.mla_kv_split(st) for st in sets]
-    run_one = binding.mla_decode_kv_split_inputs if args.kv_split else binding.mla_decode_inputs
 
     def call(i, stream):
         run_one(sets[i % len(sets)], out=out, workspace=ws, stream=stream)
 
-    wall, region, ev = _timed(call, args.steps, args.warmup)
+    wall, region, ev = _timed(call, steps, warmup)
     nbytes = synth.mla_algorithmic_bytes(cfg, seqs)
-    ntok = sum(cfg.s1 * min(int(q), cfg.topk) for q in seqs)
-    flops = 2 * (576 + 512) * cfg.nq * ntok              # S = [qn|qr].K and P.V, per query head
-    ms = wall / args.steps * 1e3
-    mean = region
+    ntok = sum(cfg.s1 * cfg.nkv * min(int(q), cfg.topk) for q in seqs)
+    flops = 2 * (576 + 512) * (cfg.nq // cfg.nkv) * ntok          # S = [qn|qr].K and P.V, per query head
+    tf = flops / (region * 1e-3) / 1e12
+    return dict(cfg=cfg, seqs=seqs, wall=wall, region=region, ev=ev, nbytes=nbytes, ntok=ntok, flops=flops,
+                entry={"workload": cfg.name + ("-kv-split" if kv_split else ""),
+                       "algorithmic_bytes_per_call": nbytes, "flop_per_call": flops,
+                       "us_per_call": round(region * 1e3, 2), "median_us": round(ev[len(ev) // 2] * 1e3, 2),
+                       "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                                    "frac": round(tf / 2500.0, 4),
+                                    "hbm_gb_s": round(nbytes / (region * 1e-3) / 1e9, 1)},
+                       "kernel": "pa::mla_decode_kernel + pa::mla_merge_kernel"})
+
+
+def secondary_entries(args):
+    """The other workloads, each timed like the headline (event-timed region over
+    rotating input sets), for the same JSON line."""
+    st, wu, rot = args.secondary_steps, 10, max(1, args.rotate)
+    sec = {}
+    for key, cid, causal in (("config2", 2, False), ("config3", 3, False), ("config3_causal", 3, True)):
+        sec[key] = measure_gqa(cid, causal, st, wu, rot)
+    sec["config4_mla"] = measure_mla(False, st, wu, rot)["entry"]
+    sec["config4_mla_kv_split"] = measure_mla(True, st, wu, rot)["entry"]
+    return sec
+
+
+def run_ceiling(args):
+    """Read-only probes beside the decode on config 1's workload: the bytes the decode
+    must read, in its paged layout, with nothing computed (the access pattern's
+    ceiling), and a contiguous read of a buffer of the same size."""
+    import ctypes
+    import torch
+    from fp8_paged_kv_amd import binding, build, synth
+    lib_path = build.PROBE_LIB
+    if not os.path.exists(lib_path):
+        sys.exit(f"{lib_path} is missing: build it with fp8_paged_kv_amd.build.build_probe()")
+    P = ctypes.CDLL(lib_path)
+    vp = ctypes.c_void_p
+    P.pa_probe_paged_read.argtypes = [vp] * 5 + [ctypes.c_int] * 6 + [vp, vp]
+    P.pa_probe_paged_read.restype = ctypes.c_int
+    P.pa_probe_contiguous_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp, vp]
+    P.pa_probe_contiguous_read.restype = ctypes.c_int
+    cfg = synth.CONFIGS[1]
+    sets, seqs = make_sets(cfg, max(1, args.rotate))
+    nbytes = synth.gqa_algorithmic_bytes(cfg, seqs)
+    blk_tok = sum((q + 127) // 128 * 128 for q in seqs)
+    paged_bytes = blk_tok * cfg.nkv * (2 * cfg.D + 4)             # whole blocks of K, V and k_scale
+    sink = torch.empty(cfg.B * cfg.nkv // 2 * cfg.max_blocks_per_seq, dtype=torch.int32, device="cuda")
+
+    def paged_probe(pgrid, nh=2):
+        def call(i, stream):
+            d = sets[i % len(sets)]
+            rc = P.pa_probe_paged_read(d["k_cache"].data_ptr(), d["k_scale"].data_ptr(), d["v_cache"].data_ptr(),
+                                       d["block_table"].data_ptr(), d["kv_act_seqs"].data_ptr(), cfg.B, cfg.nkv,
+                                       cfg.max_blocks_per_seq, cfg.num_blocks, pgrid, nh, sink.data_ptr(),
+                                       ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+        return _timed(call, args.steps, args.warmup)[1]
+
+    paged = {f"one workgroup per block of {nh} KV heads": paged_probe(0, nh) for nh in (2, 4, 8)}
+    for pg in (256, 1024):
+        paged[f"{pg} persistent workgroups, 2 KV heads per item"] = paged_probe(pg)
+    n16 = paged_bytes // 16
+    bufs = [torch.empty(n16 * 16, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(max(1, args.rotate))]
+    csink = torch.empty(256 * 16, dtype=torch.int32, device="cuda")
+
+    def contiguous_probe(grid, unroll):
+        def call(i, stream):
+            rc = P.pa_probe_contiguous_read(bufs[i % len(bufs)].data_ptr(), n16, grid, unroll, csink.data_ptr(),
+                                            ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+        return _timed(call, args.steps, args.warmup)[1]
+
+    contig = {}
+    for grid in (256, 512, 1024, 2048, 4096):
+        for unroll in (4, 8):
+            contig[f"{grid} workgroups, {unroll} loads in flight"] = contiguous_probe(grid, unroll)
+    out = torch.empty((cfg.B, cfg.nq, cfg.D), dtype=torch.bfloat16, device="cuda")
+    need, _ = binding.workspace_size(cfg.B, 1, cfg.nq, cfg.nkv, cfg.D, 128, cfg.max_blocks_per_seq, cfg.s2_tile, 0)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    _, r_dec, _ = time_calls(binding, sets, args.steps, args.warmup, 0, out, ws)
+    line = {
+        "metric": "read-only ceilings of the paged decode's access pattern, GB/s",
+        "config": {"workload": cfg.name, "rotating_input_sets": len(sets), "algorithmic_bytes_per_call": nbytes,
+                   "paged_probe_bytes": paged_bytes},
+        "paged_probe": {k: {"us": round(v * 1e3, 2), "gb_s": round(paged_bytes / (v * 1e-3) / 1e9, 1)}
+                        for k, v in paged.items()},
+        "paged_probe_note": "items = (batch, group of KV heads, valid 128-token block): the group's K and V "
+                            "slices of the 128 token rows and its k_scale words, XOR-folded, nothing computed",
+        "best_paged_2_heads_gb_s": round(paged_bytes / (paged["one workgroup per block of 2 KV heads"] * 1e-3) / 1e9,
+                                         1),
+        "contiguous_probe": {k: {"us": round(v * 1e3, 2), "gb_s": round(paged_bytes / (v * 1e-3) / 1e9, 1)}
+                             for k, v in contig.items()},
+        "contiguous_probe_note": "the same byte count read from one contiguous buffer, 16-byte loads",
+        "best_paged_gb_s": round(paged_bytes / (min(paged.values()) * 1e-3) / 1e9, 1),
+        "best_contiguous_gb_s": round(paged_bytes / (min(contig.values()) * 1e-3) / 1e9, 1),
+        "decode": {"us": round(r_dec * 1e3, 2), "gb_s": round(nbytes / (r_dec * 1e-3) / 1e9, 1),
+                   "kernel": "pa::decode_rows_kernel + pa::merge_rows_kernel"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_mla(args):
+    """The MLA-style sparse decode workload (B=16, nq=128, topk 2048, seq 4k-32k)."""
+    m = measure_mla(args.kv_split, args.steps, args.warmup, args.rotate)
+    cfg, ms = m["cfg"], m["wall"] / args.steps * 1e3
     line = {
         "metric": "MLA sparse decode, algorithmic GB/s and bf16 TFLOP/s",
-        "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(m["nbytes"] / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 MFMA on dequantised fp8 (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "s1": cfg.s1, "nq": cfg.nq, "topk": cfg.topk,
-                   "s2_tile": cfg.s2_tile, "algorithmic_bytes_per_call": nbytes, "flop_per_call": flops,
+        "config": {"workload": m["entry"]["workload"], "B": cfg.B, "s1": cfg.s1, "nq": cfg.nq, "nkv": cfg.nkv,
+                   "topk": cfg.topk, "s2_tile": cfg.s2_tile, "algorithmic_bytes_per_call": m["nbytes"],
+                   "flop_per_call": m["flops"],
                    "layout": "kv_split (three tensors)" if args.kv_split else "packed 672-byte rows"},
-        "event_us_per_call_timed_region": round(region * 1e3, 2),
-        "event_us_per_call": {"mean": round(sum(ev) / len(ev) * 1e3, 2), "median": round(ev[len(ev) // 2] * 1e3, 2),
+        "event_us_per_call_timed_region": round(m["region"] * 1e3, 2),
+        "event_us_per_call": {"mean": round(sum(m["ev"]) / len(m["ev"]) * 1e3, 2),
+                              "median": round(m["ev"][len(m["ev"]) // 2] * 1e3, 2),
                               "note": "separate pass, one event pair around each call"},
-        "tflop_s": round(flops / (mean * 1e-3) / 1e12, 2),
-        "roofline": {"bound": "mfma", "achieved": round(flops / (mean * 1e-3) / 1e12, 2), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(flops / (mean * 1e-3) / 1e12 / 2500.0, 4), "traffic": None,
-                     "hbm_gb_s": round(nbytes / (mean * 1e-3) / 1e9, 1),
-                     "kernel": "pa::mla_decode_kernel + pa::mla_merge_kernel"},
+        "tflop_s": m["entry"]["roofline"]["achieved"],
+        "roofline": dict(m["entry"]["roofline"], traffic=None, kernel=m["entry"]["kernel"]),
         # a gathered row is 656 used bytes of a 672-byte cache row
-        "row_stride": {"bytes_per_call": nbytes + ntok * (672 - 656),
-                       "ratio_to_algorithmic": round((nbytes + ntok * (672 - 656)) / nbytes, 4)},
+        "row_stride": {"bytes_per_call": m["nbytes"] + m["ntok"] * (672 - 656),
+                       "ratio_to_algorithmic": round((m["nbytes"] + m["ntok"] * (672 - 656)) / m["nbytes"], 4)},
     }
     print(json.dumps(line), flush=True)
 

@@ -65,6 +65,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(CSRC, "probe", "pa_probe_stream.hip")
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
+
+
+def build_probe() -> str:
+    """Always recompiles the bandwidth probes (a measurement tool beside the decode
+    library, not part of its ABI); writes fp8_paged_kv_amd/libpa_probe.so."""
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on the probes:\n" + r.stdout + r.stderr)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def scratch_kernels(remarks: str) -> list:
     """Names of kernels whose resource-usage remark reports a nonzero ScratchSize."""
     out, name = [], None
@@ -81,3 +98,4 @@ def scratch_kernels(remarks: str) -> list:
 
 if __name__ == "__main__":
     print(build())
+    print(build_probe())

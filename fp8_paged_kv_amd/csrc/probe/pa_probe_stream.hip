@@ -1,0 +1,177 @@
+// Bandwidth probes for the paged FP8 decode's memory access pattern (a
+// measurement tool beside the decode library, not part of its ABI).
+//
+// Each probe reads bytes and folds them into one XOR word per workgroup
+// (written to `sink`), so the loads cannot be dropped; nothing else is
+// computed.  They give the read rate the hardware sustains for:
+//  * probe_paged_kernel: the bytes the decode must read, in the decode's cache
+//    layout -- for every (batch, pair of KV heads, 128-token block) of the
+//    valid blocks, the 256-byte K and V slices of the pair in each of the 128
+//    token rows and the pair's two k_scale words per token -- one workgroup per
+//    such block (blocks past a sequence exit at once), the hardware
+//    dispatcher balancing the load;
+//  * probe_contiguous_kernel: a plain contiguous read of a buffer with 16-byte
+//    loads, grid-strided.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t fold_wg(uint32_t x, uint32_t* red) {
+    for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    uint32_t r = 0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r ^= red[i];
+    return r;
+}
+
+// grid = B * (nkv / NH) * max_blocks, 256 threads.  Workgroup (v, blk): batch
+// v / NG, KV heads NH (v % NG) .. + NH - 1, block blk of the sequence: the NH
+// heads' K and V slices (NH * 128 contiguous bytes of each token row) and their
+// k_scale words, 16 loads in flight per thread.
+template <int NH>
+__global__ __launch_bounds__(256) void probe_paged_kernel(const uint8_t* k_cache, const float* k_scale,
+                                                          const uint8_t* v_cache, const int32_t* table,
+                                                          const int32_t* seqs, int nkv, int max_blocks,
+                                                          int num_blocks, uint32_t* sink) {
+    __shared__ uint32_t red[4];
+    constexpr int PPT = NH * 8;                           // 16-byte pieces per token slice
+    const int NG = nkv / NH;
+    const int blk = blockIdx.x % max_blocks, v = blockIdx.x / max_blocks;
+    const int b = v / NG, h0 = NH * (v % NG);
+    const int seq = seqs[b];
+    if (blk * 128 >= seq) return;
+    int id = table[(int64_t)b * max_blocks + blk];
+    id = (id < 0 || id >= num_blocks) ? 0 : id;
+    const int64_t tok_stride = (int64_t)nkv * 128;
+    const uint8_t* kb = k_cache + (int64_t)id * 128 * tok_stride + h0 * 128;
+    const uint8_t* vb = v_cache + (int64_t)id * 128 * tok_stride + h0 * 128;
+    uint32_t x = 0;
+#pragma unroll
+    for (int r0 = 0; r0 < NH / 2; ++r0) {                // rounds of 8 K + 8 V pieces per thread
+        u32x4 kv[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = (r0 * 8 + i) * 256 + threadIdx.x;
+            const int t = piece / PPT, o = (piece % PPT) * 16;
+            kv[i] = *reinterpret_cast<const u32x4*>(kb + t * tok_stride + o);
+            kv[8 + i] = *reinterpret_cast<const u32x4*>(vb + t * tok_stride + o);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x ^= kv[i][0] ^ kv[i][1] ^ kv[i][2] ^ kv[i][3];
+    }
+#pragma unroll
+    for (int j = 0; j < NH / 2; ++j) {
+        const int w = j * 256 + threadIdx.x;              // k_scale word: token w / NH, head w % NH
+        x ^= __float_as_uint(k_scale[((int64_t)id * 128 + w / NH) * nkv + h0 + w % NH]);
+    }
+    const uint32_t r = fold_wg(x, red);
+    if (threadIdx.x == 0) sink[blockIdx.x] = r;
+}
+
+// U 16-byte loads in flight per thread
+template <int U>
+__global__ __launch_bounds__(256) void probe_contiguous_kernel(const u32x4* p, int64_t n16, uint32_t* sink) {
+    __shared__ uint32_t red[4];
+    uint32_t x = 0;
+    const int64_t stride = (int64_t)gridDim.x * 256 * U;
+    for (int64_t i = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i < n16; i += stride) {
+        u32x4 a[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) a[j] = (i + j * 256 < n16) ? p[i + j * 256] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < U; ++j) x ^= a[j][0] ^ a[j][1] ^ a[j][2] ^ a[j][3];
+    }
+    const uint32_t r = fold_wg(x, red);
+    if (threadIdx.x == 0) sink[blockIdx.x] = r;
+}
+
+// Persistent form of probe_paged_kernel: `gridDim.x` workgroups walk the
+// (batch, KV-head pair, block) items with a stride, the next item's loads issued
+// before the current one is folded.
+__global__ __launch_bounds__(256) void probe_paged_persistent_kernel(const uint8_t* k_cache, const float* k_scale,
+                                                                     const uint8_t* v_cache, const int32_t* table,
+                                                                     const int32_t* seqs, int nkv, int max_blocks,
+                                                                     int num_blocks, int items, uint32_t* sink) {
+    __shared__ uint32_t red[4];
+    const int NG = nkv / 2;
+    const int64_t tok_stride = (int64_t)nkv * 128;
+    uint32_t x = 0;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int blk = it % max_blocks, v = it / max_blocks;
+        const int b = v / NG, h0 = 2 * (v % NG);
+        if (blk * 128 >= seqs[b]) continue;
+        int id = table[(int64_t)b * max_blocks + blk];
+        id = (id < 0 || id >= num_blocks) ? 0 : id;
+        const uint8_t* kb = k_cache + (int64_t)id * 128 * tok_stride + h0 * 128;
+        const uint8_t* vb = v_cache + (int64_t)id * 128 * tok_stride + h0 * 128;
+        u32x4 kv[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = i * 256 + threadIdx.x;
+            const int t = piece >> 4, o = (piece & 15) * 16;
+            kv[i] = *reinterpret_cast<const u32x4*>(kb + t * tok_stride + o);
+            kv[8 + i] = *reinterpret_cast<const u32x4*>(vb + t * tok_stride + o);
+        }
+        const float ks = k_scale[((int64_t)id * 128 + (threadIdx.x >> 1)) * nkv + h0 + (threadIdx.x & 1)];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x ^= kv[i][0] ^ kv[i][1] ^ kv[i][2] ^ kv[i][3];
+        x ^= __float_as_uint(ks);
+    }
+    const uint32_t r = fold_wg(x, red);
+    if (threadIdx.x == 0) sink[blockIdx.x] = r;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Paged-pattern read probe.  persistent_grid == 0: one workgroup per item of
+// heads_per_item (2, 4 or 8) KV heads (sink: B * (nkv / heads_per_item) *
+// max_blocks words); else (heads_per_item 2) that many workgroups walk the items
+// (sink: persistent_grid words).  nkv a multiple of heads_per_item.  Returns 0 or
+// a hipError_t.
+int pa_probe_paged_read(const uint8_t* k_cache, const float* k_scale, const uint8_t* v_cache, const int32_t* table,
+                        const int32_t* seqs, int B, int nkv, int max_blocks, int num_blocks, int persistent_grid,
+                        int heads_per_item, uint32_t* sink, void* stream) {
+    const int nh = heads_per_item;
+    if (B <= 0 || nkv <= 0 || max_blocks <= 0 || num_blocks <= 0 || persistent_grid < 0 ||
+        (nh != 2 && nh != 4 && nh != 8) || nkv % nh || (persistent_grid > 0 && nh != 2))
+        return (int)hipErrorInvalidValue;
+    const int64_t items = (int64_t)B * (nkv / nh) * max_blocks;
+    if (items > 0x7fffffff) return (int)hipErrorInvalidValue;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (persistent_grid == 0 && nh == 2)
+        hipLaunchKernelGGL(probe_paged_kernel<2>, dim3((unsigned)items), dim3(256), 0, st, k_cache, k_scale, v_cache,
+                           table, seqs, nkv, max_blocks, num_blocks, sink);
+    else if (persistent_grid == 0 && nh == 4)
+        hipLaunchKernelGGL(probe_paged_kernel<4>, dim3((unsigned)items), dim3(256), 0, st, k_cache, k_scale, v_cache,
+                           table, seqs, nkv, max_blocks, num_blocks, sink);
+    else if (persistent_grid == 0)
+        hipLaunchKernelGGL(probe_paged_kernel<8>, dim3((unsigned)items), dim3(256), 0, st, k_cache, k_scale, v_cache,
+                           table, seqs, nkv, max_blocks, num_blocks, sink);
+    else
+        hipLaunchKernelGGL(probe_paged_persistent_kernel, dim3(persistent_grid), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), k_cache, k_scale, v_cache, table, seqs, nkv, max_blocks,
+                           num_blocks, (int)items, sink);
+    return (int)hipGetLastError();
+}
+
+// Contiguous read probe of n16 16-byte words with `grid` workgroups and `unroll`
+// (4 or 8) loads in flight per thread; sink: grid words.
+int pa_probe_contiguous_read(const void* p, int64_t n16, int grid, int unroll, uint32_t* sink, void* stream) {
+    if (n16 <= 0 || grid <= 0 || (unroll != 4 && unroll != 8)) return (int)hipErrorInvalidValue;
+    if (unroll == 4)
+        hipLaunchKernelGGL(probe_contiguous_kernel<4>, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const u32x4*>(p), n16, sink);
+    else
+        hipLaunchKernelGGL(probe_contiguous_kernel<8>, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const u32x4*>(p), n16, sink);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -48,7 +48,7 @@ def test_cpu_baseline_fields_on_the_small_workload():
     cfg = synth.CONFIGS[0]
     inp = synth.make_gqa_inputs(cfg)
     seqs = inp["kv_act_seqs"].tolist()
-    r = bench.cpu_baseline(cfg, [inp], seqs, target_s=5.0)
+    r = bench.cpu_baseline(cfg, inp, seqs, target_s=5.0)
     assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
     assert 1 <= r["cores"] <= 16
     assert "sequences 0..1 of 2" in r["sample"]                       # both sequences fit the budget
