@@ -291,12 +291,33 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def measure_gqa(cfg_id, causal, steps, warmup, rotate):
+def prefill_config():
+    """A chunked-prefill workload of the GLM-4.5 head layout: 128 new tokens at the
+    end of each of 4 sequences of U[2048, 8192] tokens, causal (position s sees the
+    first seq - 128 + 1 + s tokens)."""
+    from fp8_paged_kv_amd import synth
+    return synth.GqaConfig("prefill-chunk-b4-s1-128-nq96-nkv8-seq2k-8k", B=4, s1=128, nq=96, nkv=8,
+                           seq_range=(2048, 8192), s2_tile=512, num_blocks=4 * 64, max_blocks_per_seq=64,
+                           outlier_frac=0.01, seed=5)
+
+
+def causal_flops(cfg, seqs):
+    """Both contractions over the tokens each query row sees (causal limits)."""
+    G = cfg.nq // cfg.nkv
+    tok = 0
+    for sq in seqs:
+        for s in range(cfg.s1):
+            tok += max(0, min(sq - cfg.s1 + 1 + s, sq))
+    return 4 * cfg.D * G * cfg.nkv * tok
+
+
+def measure_gqa(cfg_id, causal, steps, warmup, rotate, cfg=None):
     """Event-timed decode calls on one GQA workload (rotating input sets):
-    algorithmic bytes, us per call and the HBM roofline fraction."""
+    algorithmic bytes, us per call and the HBM roofline fraction (the bf16 MFMA one
+    for prefill-length s1, where the contractions dominate)."""
     import torch
     from fp8_paged_kv_amd import binding, synth
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = cfg or synth.CONFIGS[cfg_id]
     sets, seqs = make_sets(cfg, rotate)
     for st in sets:
         st["causal"] = causal
@@ -309,12 +330,22 @@ def measure_gqa(cfg_id, causal, steps, warmup, rotate):
     del sets
     torch.cuda.empty_cache()
     gbs = nbytes / (region * 1e-3) / 1e9
-    return {"workload": cfg.name + ("-causal" if causal else ""), "algorithmic_bytes_per_call": nbytes,
-            "us_per_call": round(region * 1e3, 2), "median_us": round(ev[len(ev) // 2] * 1e3, 2),
-            "calls_per_s": round(1e3 / region, 1),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)},
-            "kernel": "pa::decode_rows_kernel + pa::merge_rows_kernel"}
+    rows = cfg.s1 * cfg.nq // cfg.nkv
+    whole_row = rows <= 32
+    entry = {"workload": cfg.name + ("-causal" if causal else ""), "algorithmic_bytes_per_call": nbytes,
+             "us_per_call": round(region * 1e3, 2), "median_us": round(ev[len(ev) // 2] * 1e3, 2),
+             "calls_per_s": round(1e3 / region, 1),
+             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4)},
+             "kernel": ("pa::decode_rows_kernel + pa::merge_rows_kernel" if whole_row else "pa::decode_kernel")}
+    if not whole_row:
+        flops = causal_flops(cfg, seqs) if causal else 4 * cfg.D * cfg.s1 * cfg.nq * sum(seqs)
+        tf = flops / (region * 1e-3) / 1e12
+        entry["flop_per_call"] = flops
+        entry["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                             "frac": round(tf / 2500.0, 4), "hbm_gb_s": round(gbs, 1),
+                             "note": "exact FP8 products on the bf16 MFMA: its dense peak"}
+    return entry
 
 
 def measure_mla(kv_split, steps, warmup, rotate):
@@ -358,6 +389,7 @@ def secondary_entries(args):
     sec = {}
     for key, cid, causal in (("config2", 2, False), ("config3", 3, False), ("config3_causal", 3, True)):
         sec[key] = measure_gqa(cid, causal, st, wu, rot)
+    sec["prefill_causal_s1_128"] = measure_gqa(None, True, max(5, st // 10), 3, 1, cfg=prefill_config())
     sec["config4_mla"] = measure_mla(False, st, wu, rot)["entry"]
     sec["config4_mla_kv_split"] = measure_mla(True, st, wu, rot)["entry"]
     return sec

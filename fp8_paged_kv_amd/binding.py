@@ -50,7 +50,7 @@ def lib():
         L.pa_fp8_decode.restype = I
         L.pa_fp8_decode_noalloc.argtypes = [P] * 9 + [I] * 6 + [F] + [I] * 4 + [P]
         L.pa_fp8_decode_noalloc.restype = I
-        L.pa_fp8_decode_causal.argtypes = [P] * 9 + [I] * 6 + [F] + [I] * 3 + [P, Z, P]
+        L.pa_fp8_decode_causal.argtypes = [P] * 9 + [I] * 6 + [F] + [I] * 4 + [P, Z, P]
         L.pa_fp8_decode_causal.restype = I
         L.pa_fp8_decode_debug.argtypes = gqa + [P, P, P]
         L.pa_fp8_decode_debug.restype = I
@@ -138,12 +138,10 @@ def decode(q, q_scale, k_cache, k_scale, v_cache, v_scale, block_table, kv_act_s
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if causal:
-        if num_splits:
-            raise ValueError("causal decode takes num_splits = 0")
         _check(lib().pa_fp8_decode_causal(
             _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
             _ptr(block_table), _ptr(kv_act_seqs), _ptr(out), B, s1, nq, nkv, D, bs, float(softmax_scale),
-            int(s2_tile), mbps, nblk, _ptr(workspace), wbytes, _stream(stream)))
+            int(s2_tile), mbps, nblk, int(num_splits), _ptr(workspace), wbytes, _stream(stream)))
         return out
     _check(lib().pa_fp8_decode(
         _ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),

@@ -51,8 +51,8 @@ pa_status_t check_shapes(int B, int s1, int nq, int nkv, int D, int block_size, 
         return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (only 128)", block_size);
     if (!tile_supported(s2_tile))
         return fail(PA_ERR_UNSUPPORTED, "s2_tile %d not built (128, 256, 512, 1024, 2048)", s2_tile);
-    if ((int64_t)s1 * (nq / nkv) > 64)
-        return fail(PA_ERR_UNSUPPORTED, "s1 * nq / nkv = %lld query rows per KV head exceeds 64",
+    if ((int64_t)s1 * (nq / nkv) > (int64_t)65535 * 32)
+        return fail(PA_ERR_UNSUPPORTED, "s1 * nq / nkv = %lld query rows per KV head exceeds 65535 * 32",
                     (long long)s1 * (nq / nkv));
     if ((int64_t)max_blocks * block_size > (int64_t)1 << 30)
         return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size exceeds 2^30 tokens");
@@ -66,9 +66,9 @@ pa_status_t check_shapes(int B, int s1, int nq, int nkv, int D, int block_size, 
 // lengths: splits beyond a sequence exit at once.  Aim for enough workgroups
 // to keep every CU streaming; more than one split is rounded to a multiple of
 // 8 (the placement spreads splits over the 8 XCDs).
-int plan_splits(int B, int nkv, int max_tiles, int requested) {
+int plan_splits(int B, int nkv, int row_blocks, int max_tiles, int requested) {
     if (requested > 0) return requested < max_tiles ? requested : max_tiles;
-    const int64_t units = (int64_t)B * nkv;
+    const int64_t units = (int64_t)B * nkv * row_blocks;
     const int64_t target = 2048;                  // launched workgroups to aim for
     int64_t s = (target + units - 1) / units;
     if (s <= 1) return 1;
@@ -78,6 +78,14 @@ int plan_splits(int B, int nkv, int max_tiles, int requested) {
 }
 
 int rows_pad(int s1, int nq, int nkv) { return (s1 * (nq / nkv) + 15) / 16 * 16; }
+
+// Per-head path: query rows per workgroup -- all of a KV head's rows (padded to 16)
+// up to 64, else blocks of 32 -- and the number of such blocks per KV head.
+int head_row_block(int s1, int nq, int nkv) { const int rp = rows_pad(s1, nq, nkv); return rp <= 64 ? rp : 32; }
+int head_row_blocks(int s1, int nq, int nkv) {
+    const int rb = head_row_block(s1, nq, nkv);
+    return (s1 * (nq / nkv) + rb - 1) / rb;
+}
 
 // CUs of the current device, queried once per device (the only state the library keeps).
 int device_cus() {
@@ -134,7 +142,7 @@ struct WorkspaceLayout {
     size_t meta, tags, part_ml, part_o, total;   // meta: arrival counters (per-head path) or the partition
 };
 
-// Per-head path with splits: [B*nkv int32 counters | pad][B*nkv*nsplit*R*2 | pad][B*nkv*nsplit*R*128]
+// Per-head path with splits: [U int32 counters | pad][U*nsplit*R*2 | pad][U*nsplit*R*128], U = B*nkv*row blocks
 // Whole-row path:             [B*nkv int32, untouched | pad][B*nkv+2 int32 partition | pad]
 //                             [256*2 int32 slot tags | pad][256*2*HG*R*2 | pad][256*2*HG*R*128]
 // with two partial slots per workgroup (its first and last segment, the only ones that can
@@ -154,7 +162,7 @@ WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit, bool rows
         return l;
     }
     if (nsplit <= 1) return l;
-    const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
+    const size_t units = (size_t)B * nkv * head_row_blocks(s1, nq, nkv), R = (size_t)head_row_block(s1, nq, nkv);
     l.meta = 0;
     l.part_ml = align256(units * sizeof(int32_t));
     l.part_o = l.part_ml + align256(units * nsplit * R * 2 * sizeof(float));
@@ -182,10 +190,8 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     const int capacity = max_blocks * block_size;
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
     const bool rows = use_rows_path(B, s1, nq, nkv, s2_tile, num_splits);
-    if (causal && !rows)
-        return fail(PA_ERR_UNSUPPORTED, "causal decode runs on the whole-row path only: num_splits must be 0, "
-                    "at most 32 query rows per KV head, s2_tile 128-1024");
-    const int nsplit = rows ? 1 : plan_splits(B, nkv, max_tiles, num_splits);
+    const int rblocks = rows ? 1 : head_row_blocks(s1, nq, nkv);
+    const int nsplit = rows ? 1 : plan_splits(B, nkv, rblocks, max_tiles, num_splits);
     const int tps = (max_tiles + nsplit - 1) / nsplit;
     const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit, rows);
     const size_t need = lay.total;
@@ -195,6 +201,8 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     const int nsplit_pad = nsplit == 1 ? 1 : (nsplit + 7) / 8 * 8;
     if ((int64_t)((B + 7) / 8 * 8) * nsplit_pad * nkv > 0x7fffffff)
         return fail(PA_ERR_UNSUPPORTED, "grid too large");
+    if ((int64_t)B * nkv * rblocks * nsplit > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "too many (batch, KV head, row block, split) units");
 
     pa::DecodeParams p;
     std::memset(&p, 0, sizeof(p));
@@ -233,13 +241,15 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.nsplit = nsplit;
     p.nsplit_pad = nsplit_pad;
     p.tiles_per_split = tps;
+    p.row_block = rows ? rows_pad(s1, nq, nkv) : head_row_block(s1, nq, nkv);
+    p.row_blocks = rblocks;
     p.softmax_scale = softmax_scale;
     p.causal = causal ? 1 : 0;
 
     hipError_t e;
     if (clear_counters && p.counters) {
         // a workspace the caller did not zero (the library's scratch): clear the arrival counters
-        const int n = B * nkv;
+        const int n = B * nkv * rblocks;
         hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
                            p.counters, n);
         e = hipGetLastError();
@@ -342,7 +352,7 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
     const int capacity = max_blocks_per_seq * block_size;
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
     const bool rows = use_rows_path(B, s1, nq, nkv, s2_tile, num_splits);
-    const int nsplit = rows ? 1 : plan_splits(B, nkv, max_tiles, num_splits);
+    const int nsplit = rows ? 1 : plan_splits(B, nkv, head_row_blocks(s1, nq, nkv), max_tiles, num_splits);
     *bytes_host = layout_for(B, s1, nq, nkv, nsplit, rows).total;
     if (splits_host) *splits_host = nsplit;
     return PA_OK;
@@ -405,12 +415,12 @@ pa_status_t pa_fp8_decode_causal(const void* q_dev, const float* q_scale_dev, co
                                  const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,
                                  const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev, void* out_dev,
                                  int B, int s1, int nq, int nkv, int D, int block_size, float softmax_scale,
-                                 int s2_tile, int max_blocks_per_seq, int num_blocks, void* workspace_dev,
-                                 size_t workspace_bytes, void* stream) {
+                                 int s2_tile, int max_blocks_per_seq, int num_blocks, int num_splits,
+                                 void* workspace_dev, size_t workspace_bytes, void* stream) {
     return run(q_dev, q_scale_dev, k_cache_dev, k_scale_dev, v_cache_dev, v_scale_dev, block_table_dev,
                kv_act_seqs_dev, out_dev, B, s1, nq, nkv, D, block_size, softmax_scale, s2_tile,
-               max_blocks_per_seq, num_blocks, 0, workspace_dev, workspace_bytes, nullptr, nullptr, false, true,
-               stream);
+               max_blocks_per_seq, num_blocks, num_splits, workspace_dev, workspace_bytes, nullptr, nullptr, false,
+               true, stream);
 }
 
 pa_status_t pa_fp8_mla_workspace_size(int B, int s1, int nq, int topk, int s2_tile, size_t* bytes_host) {

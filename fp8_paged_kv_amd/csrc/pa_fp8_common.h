@@ -31,7 +31,8 @@ struct DecodeParams {
     int B, s1, nq, nkv, G, rows;
     int s2_tile, max_blocks, num_blocks, capacity;
     int nsplit, nsplit_pad, tiles_per_split;
-    int causal;                 // whole-row path: position s of s1 sees the first seq - s1 + 1 + s tokens
+    int row_block, row_blocks;  // per-head path: query rows per workgroup (16..64) and blocks of them per KV head
+    int causal;                 // position s of s1 sees the first seq - s1 + 1 + s tokens
     float softmax_scale;
 };
 

@@ -113,18 +113,28 @@ void decode_kernel(DecodeParams a) {
     const Placement pl = place(blockIdx.x, a.B, a.nsplit, a.nsplit_pad, a.nkv);
     if (pl.empty) return;
     const int b = pl.b, sp = pl.sp, h = pl.h;
+    // query rows [r0, rend) of KV head h: one block of R rows per blockIdx.y
+    const int r0 = (int)blockIdx.y * R, rend = min(r0 + R, a.rows);
 
     int seq = a.seqs[b];
     seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
-    const int ntiles = (seq + T - 1) / T;
+    // tokens row r attends to: all of [0, seq), or with causal decode the first
+    // seq - s1 + 1 + s of them (s = r / G, its query position)
+    auto row_lim = [&](int r) -> int {
+        if (!a.causal) return seq;
+        const int n = seq - a.s1 + 1 + r / a.G;
+        return n < 0 ? 0 : (n > seq ? seq : n);
+    };
+    const int seq_lo = row_lim(r0), seq_hi = row_lim(rend - 1);   // rows see nondecreasing prefixes
+    const int ntiles = (seq_hi + T - 1) / T;
     const int t_begin = sp * a.tiles_per_split;
     const int t_end = min(t_begin + a.tiles_per_split, ntiles);
 
-    if (seq == 0) {
-        // nothing to attend to: the rows of this (b, h) are zero
+    if (seq_hi == 0) {
+        // nothing to attend to: these rows are zero
         if (sp == 0) {
-            for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
-                const int r = e / kHeadDim, d = e % kHeadDim;
+            for (int e = threadIdx.x; e < (rend - r0) * kHeadDim; e += NW * 64) {
+                const int r = r0 + e / kHeadDim, d = e % kHeadDim;
                 const int s = r / a.G, gq = r % a.G;
                 const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
                 a.out[qrow * kHeadDim + d] = 0;
@@ -139,12 +149,14 @@ void decode_kernel(DecodeParams a) {
     // lane (lr, lg) holds row rb*16+lr, dims [16lg, 16lg+16) and [64+16lg, 64+16lg+16).
     bf16x8 qop[NRB][4];                   // operand i: codes [8i, 8i+8) of the lane's 32
     float qcoef[NRB];                     // q_scale * softmax_scale * log2 e for row lr
+    int lim[NRB];                         // tokens the lane's row attends to
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-        const int r = rb * 16 + lr;
+        const int r = r0 + rb * 16 + lr;
         uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         qcoef[rb] = 0.f;
-        if (r < a.rows) {
+        lim[rb] = r < rend ? row_lim(r) : 0;
+        if (r < rend) {
             const int s = r / a.G, gq = r % a.G;
             const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
             const float qs = a.q_scale[qrow];
@@ -172,7 +184,7 @@ void decode_kernel(DecodeParams a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qop[rb][i] = fp8x8_to_op(wds[2 * i], wds[2 * i + 1]);
     }
-    if (seq == 0) return;                 // debug dump of Q only
+    if (seq_hi == 0) return;              // debug dump of Q only
 
     const int64_t tok_stride = (int64_t)a.nkv * kHeadDim;      // bytes between tokens of one head
     const uint8_t* kbase = a.k_cache + (int64_t)h * kHeadDim;
@@ -184,7 +196,7 @@ void decode_kernel(DecodeParams a) {
     // of it is wave-uniform (scalar registers).
     auto chunk_slot = [&](int t, int c) -> int64_t {
         const int p0 = t * T + w * TW + 32 * c;
-        if (t >= t_end || p0 >= seq) return -1;
+        if (t >= t_end || p0 >= seq_hi) return -1;
         int id = trow[p0 / kBlock];
         id = (id < 0 || id >= a.num_blocks) ? 0 : id;
         return (int64_t)id * kBlock + (p0 % kBlock);
@@ -273,7 +285,7 @@ void decode_kernel(DecodeParams a) {
             Chunk& ch = ring[u % kRing];
             const int c = u < CPW ? u : u - CPW;
             const int p0 = wlo + 32 * c;
-            const bool valid = p0 < seq;
+            const bool valid = p0 < seq_hi;
 
             if (u < CPW) {
                 // ---- steps 2-4: S^T = K Q^T (exact products, FP32 sums), dequantise, mask
@@ -304,13 +316,13 @@ void decode_kernel(DecodeParams a) {
                             for (int i = 0; i < 4; ++i) sv[rb][c][4 * k + i] = acc[i] * ks[4 * k + i] * qcoef[rb];
                         }
                     }
-                    if (p0 + 32 > seq) {
-                        // the sequence ends inside this chunk: mask the tokens past it
+                    if (p0 + 32 > seq_lo) {
+                        // some row's tokens end inside this chunk: mask the tokens past each row's end
 #pragma unroll
                         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
                             for (int j = 0; j < 8; ++j)
-                                sv[rb][c][j] = (p0 + chunk_token(lg, j) < seq) ? sv[rb][c][j] : -INFINITY;
+                                sv[rb][c][j] = (p0 + chunk_token(lg, j) < lim[rb]) ? sv[rb][c][j] : -INFINITY;
                     }
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
@@ -344,15 +356,16 @@ void decode_kernel(DecodeParams a) {
                         }
                         mt_s[rb] = m;
                         // exp2 argument offset: P' = 448 * exp2(S - m_tile) = exp2(S + off);
-                        // a dropped row gets off = -inf (P' = 0, nothing added)
-                        poff[rb] = (M_s[rb] - m > kDropLog2) ? -INFINITY : kLog2_448 - m;
+                        // a dropped row, or one with no token in this tile (causal), gets
+                        // off = -inf (P' = 0, nothing added)
+                        poff[rb] = (m == -INFINITY || M_s[rb] - m > kDropLog2) ? -INFINITY : kLog2_448 - m;
                         // O <- O * exp2(M_old - m_tile): alpha if the tile raises the max,
                         // else 1/beta; the tile's P.V is then added and the sum scaled by beta.
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             mt_o[rb][i] = mo[i];
                             const float d = M_o[rb][i] - mo[i];
-                            const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(d);
+                            const float sc = (mo[i] == -INFINITY || d > kDropLog2) ? 1.f : __builtin_amdgcn_exp2f(d);
 #pragma unroll
                             for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
                         }
@@ -367,11 +380,11 @@ void decode_kernel(DecodeParams a) {
                         xl[j] = ch.w[2 * j];
                         xh[j] = ch.w[2 * j + 1];
                     }
-                    if (p0 + 32 > seq) {
-                        // tokens past the sequence: zero their V bytes (0 * NaN would poison P.V)
+                    if (p0 + 32 > seq_hi) {
+                        // tokens past the rows' last one: zero their V bytes (0 * NaN would poison P.V)
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const bool in = p0 + chunk_token(lg, j) < seq;
+                            const bool in = p0 + chunk_token(lg, j) < seq_hi;
                             xl[j] = in ? xl[j] : 0u;
                             xh[j] = in ? xh[j] : 0u;
                         }
@@ -407,15 +420,19 @@ void decode_kernel(DecodeParams a) {
                     // ---- steps 8-9: finish the rescale, update the running state --------
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb) {
-                        const float mn = fmaxf(M_s[rb], mt_s[rb]);
-                        L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) +
-                                  lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
-                        M_s[rb] = mn;
+                        // a row with no token in this tile (causal) keeps its state
+                        if (mt_s[rb] != -INFINITY) {
+                            const float mn = fmaxf(M_s[rb], mt_s[rb]);
+                            L_s[rb] = L_s[rb] * __builtin_amdgcn_exp2f(M_s[rb] - mn) +
+                                      lsum[rb] * __builtin_amdgcn_exp2f(mt_s[rb] - mn);
+                            M_s[rb] = mn;
+                        }
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float mo = fmaxf(M_o[rb][i], mt_o[rb][i]);
                             const float d = M_o[rb][i] - mt_o[rb][i];
-                            const float sc = d > kDropLog2 ? 1.f : __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
+                            const float sc = (mt_o[rb][i] == -INFINITY || d > kDropLog2)
+                                                 ? 1.f : __builtin_amdgcn_exp2f(mt_o[rb][i] - mo);
                             M_o[rb][i] = mo;
 #pragma unroll
                             for (int cc = 0; cc < 8; ++cc) O[rb][cc][i] *= sc;
@@ -448,28 +465,32 @@ void decode_kernel(DecodeParams a) {
 
     const float* vs = a.v_scale + ((int64_t)b * a.nkv + h) * kHeadDim;
     const int nact = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;   // splits with work
+    const int nrow = rend - r0;
     if (nact == 1) {
         // ---- step 10: out = O * v_scale / L' (L' = 448 L: P' = 448 P is summed), bf16 ----
-        for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
-            const int r = e / kHeadDim, d = e % kHeadDim;
+        // (a row that attends to no token at all, causal, is zero)
+        for (int e = threadIdx.x; e < nrow * kHeadDim; e += NW * 64) {
+            const int rl = e / kHeadDim, d = e % kHeadDim, r = r0 + rl;
             const int s = r / a.G, gq = r % a.G;
             const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
-            a.out[qrow * kHeadDim + d] = f32_to_bf16_rne(s_acc[r][d] * vs[d] / s_l[r]);
+            const float L = s_l[rl];
+            a.out[qrow * kHeadDim + d] = L > 0.f ? f32_to_bf16_rne(s_acc[rl][d] * vs[d] / L) : (uint16_t)0;
         }
         return;
     }
 
-    // ---- split partials, then the last split of (b, h) merges them -------------------------
-    // partial layout: [b][h][split][R rows][128] for O, [b][h][split][R][2] for (M, L)
-    const int64_t unit = (int64_t)b * a.nkv + h;
+    // ---- split partials, then the last split of the unit merges them -----------------------
+    // unit = (b, h, row block); partial layout: [unit][split][R rows][128] for O,
+    // [unit][split][R][2] for (M, L)
+    const int64_t unit = ((int64_t)b * a.nkv + h) * a.row_blocks + blockIdx.y;
     float* po = a.part_o + (unit * a.nsplit + sp) * (R * kHeadDim);
     float* pml = a.part_ml + (unit * a.nsplit + sp) * (R * 2);
-    for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) po[e] = s_acc[e / kHeadDim][e % kHeadDim];
+    for (int e = threadIdx.x; e < nrow * kHeadDim; e += NW * 64) po[e] = s_acc[e / kHeadDim][e % kHeadDim];
     if (w == 0 && lg == 0) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
             const int r = rb * 16 + lr;
-            if (r < a.rows) {
+            if (r < nrow) {
                 pml[2 * r] = M_s[rb];
                 pml[2 * r + 1] = s_l[r];
             }
@@ -489,24 +510,28 @@ void decode_kernel(DecodeParams a) {
     // log-sum-exp merge of the nact partials, in split order (deterministic)
     const float* po0 = a.part_o + (unit * a.nsplit) * (R * kHeadDim);
     const float* pml0 = a.part_ml + (unit * a.nsplit) * (R * 2);
-    for (int r = threadIdx.x; r < a.rows; r += NW * 64) {
+    for (int r = threadIdx.x; r < nrow; r += NW * 64) {
         float Ms = -INFINITY;
         for (int i = 0; i < nact; ++i) Ms = fmaxf(Ms, pml0[i * R * 2 + 2 * r]);
         float L = 0.f;
-        for (int i = 0; i < nact; ++i) L += pml0[i * R * 2 + 2 * r + 1] * __builtin_amdgcn_exp2f(pml0[i * R * 2 + 2 * r] - Ms);
+        if (Ms != -INFINITY)              // a split where the row saw nothing has M = -inf, L = 0
+            for (int i = 0; i < nact; ++i)
+                L += pml0[i * R * 2 + 2 * r + 1] * __builtin_amdgcn_exp2f(pml0[i * R * 2 + 2 * r] - Ms);
         s_l[r] = L;
         s_ms[r] = Ms;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < a.rows * kHeadDim; e += NW * 64) {
-        const int r = e / kHeadDim, d = e % kHeadDim;
-        const float Ms = s_ms[r];
+    for (int e = threadIdx.x; e < nrow * kHeadDim; e += NW * 64) {
+        const int rl = e / kHeadDim, d = e % kHeadDim, r = r0 + rl;
+        const float Ms = s_ms[rl];
         float o = 0.f;
-        for (int i = 0; i < nact; ++i)
-            o += po0[(int64_t)i * R * kHeadDim + e] * __builtin_amdgcn_exp2f(pml0[i * R * 2 + 2 * r] - Ms);
+        if (Ms != -INFINITY)
+            for (int i = 0; i < nact; ++i)
+                o += po0[(int64_t)i * R * kHeadDim + e] * __builtin_amdgcn_exp2f(pml0[i * R * 2 + 2 * rl] - Ms);
         const int s = r / a.G, gq = r % a.G;
         const int64_t qrow = ((int64_t)b * a.s1 + s) * a.nq + h * a.G + gq;
-        a.out[qrow * kHeadDim + d] = f32_to_bf16_rne(o * vs[d] / s_l[r]);
+        const float L = s_l[rl];
+        a.out[qrow * kHeadDim + d] = L > 0.f ? f32_to_bf16_rne(o * vs[d] / L) : (uint16_t)0;
     }
 }
 
@@ -520,10 +545,11 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 
 template <int NRB, int NW, int CPW>
 static hipError_t launch_nrb(const DecodeParams& p, int grid, hipStream_t st, bool dbg) {
+    const dim3 g(grid, p.row_blocks);    // (batch, split, KV head) x blocks of query rows
     if (dbg)
-        hipLaunchKernelGGL((decode_kernel<NRB, NW, CPW, true>), dim3(grid), dim3(NW * 64), 0, st, p);
+        hipLaunchKernelGGL((decode_kernel<NRB, NW, CPW, true>), g, dim3(NW * 64), 0, st, p);
     else
-        hipLaunchKernelGGL((decode_kernel<NRB, NW, CPW, false>), dim3(grid), dim3(NW * 64), 0, st, p);
+        hipLaunchKernelGGL((decode_kernel<NRB, NW, CPW, false>), g, dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
@@ -550,7 +576,7 @@ int grid_size(const DecodeParams& p) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st, bool dbg) {
-    const int nrb = (p.rows + 15) / 16;
+    const int nrb = p.row_block / 16;
     const int grid = grid_size(p);
     hipError_t e;
     if (dbg && p.dbg_rows) {

@@ -106,7 +106,7 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
  * [0, max_blocks_per_seq * block_size]; seq_b == 0 gives zero output rows;
  * bytes of tokens p >= seq_b are never used (their values may be NaN).
  * Supported: D == 128, block_size == 128, s2_tile in {128, 256, 512, 1024,
- * 2048}, s1 * nq / nkv <= 64.  num_splits: 0 = the library's choice, else
+ * 2048}, s1 * nq / nkv <= 65535 * 32.  num_splits: 0 = the library's choice, else
  * the number of contiguous tile ranges each sequence is split into (>= 1).
  * Whenever pa_fp8_decode_workspace_size reports a nonzero size,
  * workspace_dev must hold at least that many bytes.
@@ -118,10 +118,12 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
  *    s2_tile 2048 is not served) and B * ceil(nkv / 2) <= 1024 (batch, head
  *    pair) units (nkv odd: B * nkv <= 1024).
  *  - otherwise (an explicit num_splits, or a shape outside those limits,
- *    e.g. B >= 257 at nkv = 8): one workgroup per (batch, KV head, split)
- *    with the split count chosen from the table capacity.  It is the slower
- *    path for large batches of short sequences; choose shapes inside the
- *    whole-row limits where speed matters.
+ *    e.g. B >= 257 at nkv = 8, or more than 32 query rows per KV head): one
+ *    workgroup per (batch, KV head, block of query rows, split) -- all of a
+ *    KV head's rows when they are at most 64, else blocks of 32 -- with the
+ *    split count chosen from the table capacity.  It is the slower path for
+ *    large batches of short sequences; choose shapes inside the whole-row
+ *    limits where speed matters.
  */
 pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev,
                           const uint8_t* k_cache_dev, const float* k_scale_dev,
@@ -178,22 +180,25 @@ pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev,
                                 int32_t* rows_dev, uint8_t* q8_dev, void* stream);
 
 /*
- * Causal multi-token decode: pa_fp8_decode with query position s of s1
- * attending to the first n_s = clamp(seq - s1 + 1 + s, 0, seq) tokens only
- * (the s1 new tokens are the sequence's last ones and each sees itself and
- * what precedes it) -- [P2]'s valid count (section 关键实现细节) with the
- * sequence in place of topk.  Each position keeps its own tiles over [0, n_s)
- * (P quantised per row over the tile's tokens that row sees); n_s = 0 gives a
- * zero row.  Same arguments and workspace as pa_fp8_decode with
- * num_splits = 0; shapes outside the whole-row path (more than 32 query rows
- * per KV head, s2_tile 2048, very large batches) return PA_ERR_UNSUPPORTED.
+ * Causal multi-token decode and chunked prefill: pa_fp8_decode with query
+ * position s of s1 attending to the first n_s = clamp(seq - s1 + 1 + s, 0, seq)
+ * tokens only (the s1 new tokens are the sequence's last ones and each sees
+ * itself and what precedes it) -- [P2]'s valid count (section 关键实现细节)
+ * with the sequence in place of topk; [P2] section API 签名与 Decode / Prefill
+ * 差异 gives decode and prefill one signature, and so does this entry: s1 may
+ * be a prefill chunk (hundreds of positions).  Each position keeps its own
+ * tiles over [0, n_s) (P quantised per row over the tile's tokens that row
+ * sees); n_s = 0 gives a zero row.  Same arguments, workspace, split count
+ * and paths as pa_fp8_decode: the whole-row path when num_splits == 0 and the
+ * shape is inside its limits, else the per-head path, which takes any number
+ * of query rows per KV head (blocks of 32 rows when there are more than 64).
  */
 pa_status_t pa_fp8_decode_causal(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
                                  const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,
                                  const int32_t* block_table_dev, const int32_t* kv_act_seqs_dev, void* out_dev,
                                  int B, int s1, int nq, int nkv, int D, int block_size, float softmax_scale,
-                                 int s2_tile, int max_blocks_per_seq, int num_blocks, void* workspace_dev,
-                                 size_t workspace_bytes, void* stream);
+                                 int s2_tile, int max_blocks_per_seq, int num_blocks, int num_splits,
+                                 void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes pa_fp8_mla_sparse_decode needs for these sizes.

@@ -56,7 +56,7 @@ def call(lib, **over):
     (dict(q=None), 1), (dict(out=None), 1), (dict(table=None), 1),
     (dict(B=0), 2), (dict(nq=7), 2), (dict(tile=200), 2), (dict(splits=-1), 2), (dict(nblocks=0), 2),
     (dict(scale=0.0), 2), (dict(scale=float("inf")), 2), (dict(scale=float("nan")), 2),
-    (dict(D=64), 3), (dict(bs=64, tile=256), 3), (dict(tile=384), 3), (dict(s1=5, nq=32, nkv=2), 3),
+    (dict(D=64), 3), (dict(bs=64, tile=256), 3), (dict(tile=384), 3), (dict(s1=65536 * 16, nq=4, nkv=2), 3),
     (dict(splits=2, ws=None), 4), (dict(splits=2, ws=FAKE, wsb=16), 4),
 ])
 def test_host_validation_codes(lib, over, code):
@@ -132,11 +132,36 @@ def test_epilog_page_row_sizes_accepted(lib):
                                                             ctypes.byref(n)) == 2
 
 
-def test_causal_needs_the_whole_row_path(lib):
-    """More than 32 query rows per KV head (s1=2, G=32) is outside the whole-row path."""
-    rc = lib.pa_fp8_decode_causal(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 2, 128, 128,
-                                  0.088, 256, 6, 8, FAKE, 1 << 20, None)
-    assert rc == 3 and b"whole-row" in lib.pa_fp8_last_error_string()
+def causal(lib, **over):
+    a = dict(B=2, s1=2, nq=64, nkv=2, tile=256, mbps=6, nblocks=8, splits=3, ws=None, wsb=0, q=FAKE)
+    a.update(over)
+    return lib.pa_fp8_decode_causal(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["s1"], a["nq"],
+                                    a["nkv"], 128, 128, 0.088, a["tile"], a["mbps"], a["nblocks"], a["splits"],
+                                    a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(splits=-1), 2), (dict(nq=63), 2),
+    (dict(s1=65536 * 32), 3),                      # more query rows per KV head than the row blocks cover
+    (dict(ws=None), 4),                            # per-head path with 3 splits needs a workspace
+    (dict(s1=512, nq=96, nkv=8, splits=2, ws=FAKE, wsb=1024), 4),
+])
+def test_causal_host_validation_codes(lib, over, code):
+    """Causal decode takes the per-head path too (any number of query rows per
+    KV head, explicit splits); its arguments are checked like pa_fp8_decode's."""
+    assert causal(lib, **over) == code
+    assert len(lib.pa_fp8_last_error_string()) > 0
+
+
+def test_prefill_workspace_grows_with_row_blocks(lib):
+    """More than 64 query rows per KV head: blocks of 32 rows, each (batch, KV
+    head, row block) with its own partials and arrival counter."""
+    from fp8_paged_kv_amd import binding
+    n1, s1_ = binding.workspace_size(2, 8, 64, 2, 128, 128, 16, 256, 3)     # 256 rows per KV head: 8 blocks
+    n2, _ = binding.workspace_size(2, 4, 64, 2, 128, 128, 16, 256, 3)      # 128 rows: 4 blocks
+    assert s1_ == 3 and n1 > n2 > 0
+    units = 2 * 2 * 8
+    assert n1 >= units * 3 * 32 * (128 + 2) * 4
 
 
 def mla(lib, **over):

@@ -243,7 +243,61 @@ def test_causal_parity(B, oracle_mod, s1, nq, nkv, s2_tile, seqs):
                 num_blocks=mb * len(seqs), max_blocks_per_seq=mb, seed=40 + s1)
     inp = dict(synth.make_gqa_inputs(cfg), causal=True)
     ref = oracle_mod.gqa_decode(inp)
-    got = _run(B, inp, 0, "causal")
-    compare(got, ref, f"causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile}")
-    if s1 == 1:
-        assert np.array_equal(got, _run(B, dict(inp, causal=False), 0, "plain"))
+    for ns in (0, 1, 3):                     # whole-row path, per-head path without and with splits
+        got = _run(B, inp, ns, "causal")
+        compare(got, ref, f"causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile} splits={ns}")
+        if s1 == 1:
+            assert np.array_equal(got, _run(B, dict(inp, causal=False), ns, "plain"))
+
+
+def _rows_ref(oracle_mod, inp):
+    """The oracle over every output row, rows spread over the threads (few long batches)."""
+    c = inp["cfg"]
+    return oracle_mod.gqa_decode_rows(inp, np.arange(c.B * c.s1 * c.nq))
+
+
+@pytest.mark.parametrize("s1,nq,nkv,s2_tile,seqs", [
+    (128, 12, 1, 256, (700, 2000, 128, 100)),     # G = 12: 1536 query rows per KV head; seq < s1 in the last
+    (128, 96, 8, 512, (1100, 2600)),              # the GLM-4.5 head layout
+    (512, 12, 1, 512, (600, 1500, 300)),          # 6144 rows; seq 300 < s1: the first 211 positions see nothing
+    (512, 12, 1, 128, (1024, 513)),
+])
+def test_prefill_causal_parity(B, oracle_mod, s1, nq, nkv, s2_tile, seqs):
+    """Causal decode with prefill-length s1 (the page pair's Decode / Prefill
+    entries share one signature): the per-head path in blocks of 32 query rows,
+    position s seeing the first seq - s1 + 1 + s tokens; without and with
+    splits."""
+    mb = (max(seqs) + 127) // 128 + 1
+    cfg = _case(f"prefill-s1{s1}-nq{nq}", B=len(seqs), s1=s1, nq=nq, nkv=nkv, s2_tile=s2_tile, seq_lens=seqs,
+                num_blocks=mb * len(seqs), max_blocks_per_seq=mb, seed=70 + s1 + nq)
+    inp = dict(synth.make_gqa_inputs(cfg), causal=True)
+    ref = _rows_ref(oracle_mod, inp)
+    for ns in (0, 2):
+        got = _run(B, inp, ns, f"prefill s1={s1}")
+        compare(got.reshape(-1, 128), ref, f"prefill causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile} splits={ns}")
+        rows = got.reshape(len(seqs), s1, nq, 128)
+        for bi, sq in enumerate(seqs):          # positions that see no token are zero rows
+            nz = max(0, s1 - sq)
+            assert np.all(rows[bi, :nz] == 0.0)
+
+
+def test_long_s1_non_causal_parity(B, oracle_mod):
+    """More than 64 query rows per KV head without the causal limit (every
+    position attends to the whole sequence): row blocks of 32."""
+    cfg = _case("long-s1", B=3, s1=16, nq=48, nkv=4, s2_tile=256, seq_lens=(900, 77, 1400), num_blocks=40,
+                max_blocks_per_seq=12, seed=81)
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    for ns in (0, 1, 4):
+        compare(_run(B, inp, ns, "long s1"), ref, f"long s1 non-causal splits={ns}")
+
+
+@pytest.mark.parametrize("num_splits", [0, 2])
+def test_prefill_causal_poison_bit_identical(B, num_splits):
+    """NaN codes and scales past every sequence change no output bit of the
+    causal prefill either."""
+    cfg = _case("prefill-poison", B=3, s1=64, nq=12, nkv=1, s2_tile=256, seq_lens=(40, 700, 1300), num_blocks=30,
+                max_blocks_per_seq=11, seed=91)
+    clean = _run(B, dict(synth.make_gqa_inputs(cfg), causal=True), num_splits, "prefill poison clean")
+    dirty = _run(B, dict(synth.make_gqa_inputs(cfg, poison=True), causal=True), num_splits, "prefill poison dirty")
+    assert np.array_equal(clean, dirty)
