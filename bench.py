@@ -41,7 +41,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
-    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling"], default="decode",
+    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma"], default="decode",
                     help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
                          "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows; "
                          "ceiling: read-only probes of config 1's paged access pattern and of a contiguous "
@@ -182,6 +182,8 @@ def main():
         return run_epilog(args)
     if args.op == "ceiling":
         return run_ceiling(args)
+    if args.op == "fp8-mfma":
+        return run_fp8_mfma(args)
     if args.config == 4:
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
@@ -471,6 +473,91 @@ def run_ceiling(args):
                    "kernel": "pa::decode_rows_kernel + pa::merge_rows_kernel"},
     }
     print(json.dumps(line), flush=True)
+
+
+def run_fp8_mfma(args):
+    """What gfx950's FP8 MFMA (v_mfma_f32_16x16x32_fp8_fp8) returns for 16x16x32
+    products of E4M3 codes, against the exact FP64 sums, beside the bf16 MFMA on
+    the same codes decoded exactly (the contraction the decode kernels use)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from fp8_paged_kv_amd import build, synth
+    P = ctypes.CDLL(build.PROBE_LIB)
+    vp = ctypes.c_void_p
+    P.pa_probe_fp8_mfma.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
+    P.pa_probe_fp8_mfma.restype = ctypes.c_int
+    g = torch.Generator().manual_seed(11)
+
+    def finite_codes(shape):
+        c = torch.randint(0, 254, shape, generator=g, dtype=torch.int32)
+        return (c + (c >= 0x7F).to(torch.int32)).to(torch.uint8)
+
+    def e4m3(x):
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    cases = {}
+    n = 256
+    cases["uniform codes (all finite E4M3 values)"] = (finite_codes((n, 16, 32)), finite_codes((n, 16, 32)))
+    a = torch.randn((n, 16, 32), generator=g)
+    b = torch.randn((n, 16, 32), generator=g)
+    cases["N(0,1) rows scaled to amax 448"] = (e4m3(a / a.abs().amax(-1, keepdim=True) * 448),
+                                              e4m3(b / b.abs().amax(-1, keepdim=True) * 448))
+    # one large product per group of 8 beside seven small ones of the same sign
+    a = torch.full((n, 16, 32), 2.0 ** -3)
+    b = torch.full((n, 16, 32), 2.0 ** -3)
+    a[:, :, ::8] = 448.0
+    b[:, :, ::8] = 448.0
+    cases["one 448x448 product and seven 2^-6 products per group of 8"] = (e4m3(a), e4m3(b))
+    # the GLM-4.5-shaped workload's own operands: query codes q / q_scale and key codes from the cache,
+    # 32-channel slices, 12 query heads of a KV head (+4 repeated) against 16 tokens
+    cfg = synth.CONFIGS[1]
+    inp = synth.make_gqa_inputs(cfg)
+    q8 = e4m3(inp["q"].float() / inp["q_scale"][..., None])          # [B, nq, 128]
+    k8 = inp["k_cache"]                                                # [nb, 128, nkv, 128]
+    G = cfg.nq // cfg.nkv
+    table = inp["block_table"]
+    aa, bb = [], []
+    for i in range(n):
+        bi, h, sl = i % cfg.B, (i // cfg.B) % cfg.nkv, (i // (cfg.B * cfg.nkv)) % 4
+        heads = [h * G + (j % G) for j in range(16)]
+        blk = int(table[bi, 0])
+        aa.append(q8[bi, heads, 32 * sl:32 * sl + 32])
+        bb.append(k8[blk, 16 * (i % 8):16 * (i % 8) + 16, h, 32 * sl:32 * sl + 32])
+    cases["GLM-4.5-shaped workload: query codes x key codes (outlier channels x20)"] = (torch.stack(aa),
+                                                                                        torch.stack(bb))
+    report = {}
+    for name, (ca, cb) in cases.items():
+        ca, cb = ca.contiguous(), cb.contiguous()
+        cnt = ca.shape[0]
+        da, db = ca.cuda(), cb.cuda()
+        c = torch.empty((cnt, 16, 16), device="cuda")
+        cr = torch.empty_like(c)
+        rc = P.pa_probe_fp8_mfma(da.data_ptr(), db.data_ptr(), c.data_ptr(), cr.data_ptr(), cnt,
+                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: {rc}")
+        torch.cuda.synchronize()
+        va = ca.view(torch.float8_e4m3fn).double().numpy()
+        vb = cb.view(torch.float8_e4m3fn).double().numpy()
+        exact = np.einsum("nik,njk->nij", va, vb)
+        mag = np.einsum("nik,njk->nij", np.abs(va), np.abs(vb))        # sum of |products|
+        got, ref = c.cpu().double().numpy(), cr.cpu().double().numpy()
+        scale = np.maximum(np.abs(exact), 1e-30)
+        e8, eb = np.abs(got - exact), np.abs(ref - exact)
+        i8 = np.unravel_index(int(np.argmax(e8 / scale)), e8.shape)
+        report[name] = {
+            "products": int(exact.size),
+            "fp8_mfma": {"max_rel_err": float((e8 / scale).max()), "max_err_over_sum_abs": float((e8 / mag).max()),
+                         "frac_rel_err_above_1e-3": float(((e8 / scale) > 1e-3).mean()),
+                         "frac_inexact": float((e8 > 0).mean()),
+                         "worst": {"exact": float(exact[i8]), "fp8_mfma": float(got[i8])}},
+            "bf16_mfma_on_decoded_codes": {"max_rel_err": float((eb / scale).max()),
+                                           "max_err_over_sum_abs": float((eb / mag).max()),
+                                           "frac_inexact": float((eb > 0).mean())},
+        }
+    print(json.dumps({"metric": "FP8 MFMA vs exact sums, 16x16x32 products of E4M3 codes", "cases": report}),
+          flush=True)
 
 
 def run_mla(args):

@@ -126,9 +126,56 @@ __global__ __launch_bounds__(256) void probe_paged_persistent_kernel(const uint8
     if (threadIdx.x == 0) sink[blockIdx.x] = r;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// One 16x16x32 product per workgroup (one wave) on E4M3 codes: a [16 rows][32 k]
+// and b [16 columns][32 k] bytes; c [16][16] fp32 from the FP8 MFMA
+// (v_mfma_f32_16x16x32_fp8_fp8) and c_ref [16][16] from the bf16 MFMA on the
+// codes decoded exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1).
+// Lane l holds k = 8 (l / 16) .. + 8 of row / column l % 16; the result gives
+// lane l the elements [4 (l / 16) + i][l % 16].
+__global__ __launch_bounds__(64) void probe_fp8_mfma_kernel(const uint8_t* a, const uint8_t* b, float* c,
+                                                            float* c_ref) {
+    const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+    const uint8_t* ap = a + (int64_t)blockIdx.x * 512 + n * 32 + 8 * g;
+    const uint8_t* bp = b + (int64_t)blockIdx.x * 512 + n * 32 + 8 * g;
+    const uint2 av = *reinterpret_cast<const uint2*>(ap);
+    const uint2 bv = *reinterpret_cast<const uint2*>(bp);
+    const long a64 = (long)(((uint64_t)av.y << 32) | av.x), b64 = (long)(((uint64_t)bv.y << 32) | bv.x);
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 r = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a64, b64, zero, 0, 0, 0);
+    auto dec = [](uint32_t w0, uint32_t w1) {
+        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+        bf16x8 v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        return v;
+    };
+    const f32x4 rr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dec(av.x, av.y), dec(bv.x, bv.y), zero, 0, 0, 0);
+    float* cp = c + (int64_t)blockIdx.x * 256;
+    float* crp = c_ref + (int64_t)blockIdx.x * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        cp[(4 * g + i) * 16 + n] = r[i];
+        crp[(4 * g + i) * 16 + n] = rr[i];
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// FP8 MFMA probe: `count` independent 16x16x32 products (a, b: count * 512 code
+// bytes; c, c_ref: count * 256 floats).  Returns 0 or a hipError_t.
+int pa_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, float* c, float* c_ref, int count, void* stream) {
+    if (count <= 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(probe_fp8_mfma_kernel, dim3(count), dim3(64), 0, static_cast<hipStream_t>(stream), a, b, c,
+                       c_ref);
+    return (int)hipGetLastError();
+}
 
 // Paged-pattern read probe.  persistent_grid == 0: one workgroup per item of
 // heads_per_item (2, 4 or 8) KV heads (sink: B * (nkv / heads_per_item) *
