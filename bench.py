@@ -41,7 +41,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
-    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma"], default="decode",
+    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma", "phases"], default="decode",
                     help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
                          "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows; "
                          "ceiling: read-only probes of config 1's paged access pattern and of a contiguous "
@@ -184,6 +184,8 @@ def main():
         return run_ceiling(args)
     if args.op == "fp8-mfma":
         return run_fp8_mfma(args)
+    if args.op == "phases":
+        return run_phases(args)
     if args.config == 4:
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
@@ -558,6 +560,124 @@ def run_fp8_mfma(args):
         }
     print(json.dumps({"metric": "FP8 MFMA vs exact sums, 16x16x32 products of E4M3 codes", "cases": report}),
           flush=True)
+
+
+def _pct(a, q):
+    import numpy as np
+    return round(float(np.percentile(a, q)), 2)
+
+
+def run_phases(args):
+    """Per-workgroup phase times of the decode (--config 1-3, whole-row kernel) or the
+    MLA decode (--config 4), read from the phase-stamp build of the library
+    (libpa_fp8_phases.so: the same kernels and results, plus s_memrealtime stamps)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from fp8_paged_kv_amd import binding, build, synth
+    if not os.path.exists(build.PHASES_LIB):
+        sys.exit(f"{build.PHASES_LIB} is missing: build it with fp8_paged_kv_amd.build.build_phases()")
+    binding._lib = None
+    binding.LIB_PATH = build.PHASES_LIB
+    L = binding.lib()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    us = 0.01                                                  # s_memrealtime ticks (100 MHz) -> us
+    calls = max(4, min(args.steps, 20))
+    if args.config == 4:
+        L.pa_fp8_phases_mla.restype = ctypes.c_void_p
+        ptr = L.pa_fp8_phases_mla()
+        cfg = synth.CONFIGS[4]
+        first = synth.make_mla_inputs(cfg, device="cuda")
+        seqs = first["kv_act_seqs"].cpu().tolist()
+        sets = [first] + [synth.make_mla_inputs(cfg, device="cuda", seed=1000 + 17 * i + cfg.seed, seq_lens=seqs)
+                          for i in range(1, max(1, args.rotate))]
+        out = torch.empty((cfg.B * cfg.nq, 512), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(binding.mla_workspace_size(cfg.B, 1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
+                         device="cuda")
+        grid = cfg.B * cfg.s1 * ((cfg.topk + cfg.s2_tile - 1) // cfg.s2_tile) * (cfg.nq // 32)
+        names = ["rows and queries staged", "score pass", "wait for the tile maxima", "softmax, P to LDS",
+                 "P.V pass", "partial writes"]
+        for i in range(args.warmup):
+            binding.mla_decode_inputs(sets[i % len(sets)], out=out, workspace=ws)
+        torch.cuda.synchronize()
+        buf = np.zeros(4096 * 8, dtype=np.uint64)
+        rows = []
+        for i in range(calls):
+            binding.mla_decode_inputs(sets[i % len(sets)], out=out, workspace=ws)
+            torch.cuda.synchronize()
+            hip.hipMemcpy(buf.ctypes.data, ptr, buf.nbytes, 2)
+            rows.append(buf.reshape(4096, 8)[:grid, :7].astype(np.int64).copy())
+        st = np.stack(rows)                                    # [calls, wg, 7]
+        t0 = st[:, :, 0].min(axis=1, keepdims=True)
+        d = np.diff(st, axis=2) * us
+        phases = {n: {"mean": round(float(d[:, :, k].mean()), 2), "p10": _pct(d[:, :, k], 10),
+                      "p90": _pct(d[:, :, k], 90)} for k, n in enumerate(names)}
+        start, end = (st[:, :, 0] - t0) * us, (st[:, :, 6] - t0) * us
+        line = {"metric": "per-workgroup phase times, us", "config": {"workload": cfg.name, "calls": calls,
+                                                                        "workgroups": grid},
+                "kernel": "pa::mla_decode_kernel", "phases": phases,
+                "dispatch_ramp": {"mean": round(float(start.mean()), 2), "max": round(float(start.max()), 2)},
+                "workgroup_end": {"mean": round(float(end.mean()), 2), "p90": _pct(end, 90),
+                                  "max": round(float(end.max(axis=1).mean()), 2)}}
+        print(json.dumps(line), flush=True)
+        return
+    L.pa_fp8_phases_rows.restype = ctypes.c_void_p
+    ptr = L.pa_fp8_phases_rows()
+    cfg = synth.CONFIGS[args.config]
+    sets, seqs = make_sets(cfg, max(1, args.rotate))
+    out = torch.empty((cfg.B * cfg.s1, cfg.nq, cfg.D), dtype=torch.bfloat16, device="cuda")
+    need, _ = binding.workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.nkv, cfg.D, cfg.block_size, cfg.max_blocks_per_seq,
+                                     cfg.s2_tile, 0)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    for i in range(args.warmup):
+        binding.decode_inputs(sets[i % len(sets)], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    buf = np.zeros(256 * 8, dtype=np.uint64)
+    rows = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    call_us = []
+    for i in range(calls):
+        e0.record()
+        binding.decode_inputs(sets[i % len(sets)], out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        call_us.append(e0.elapsed_time(e1) * 1e3)
+        hip.hipMemcpy(buf.ctypes.data, ptr, buf.nbytes, 2)
+        rows.append(buf.reshape(256, 8).astype(np.int64).copy())
+    st = np.stack(rows)                                        # [calls, 256, 8]
+    live = st[:, :, 5] > 0                                     # workgroups that had work
+    t0 = st[:, :, 0].min(axis=1, keepdims=True)
+    ramp = (st[:, :, 0] - t0) * us
+    pro = (st[:, :, 1] - st[:, :, 0]) * us
+    first = (st[:, :, 7] - st[:, :, 1]) * us
+    loop = (st[:, :, 2] - st[:, :, 1]) * us
+    qc, ends = st[:, :, 3] * us, st[:, :, 4] * us
+    stream = loop - qc - ends
+    steps, segs = st[:, :, 5], st[:, :, 6]
+    end = (st[:, :, 2] - t0) * us
+    span = end.max(axis=1)
+
+    def stat(a):
+        a = a[live]
+        return {"mean": round(float(a.mean()), 2), "p10": _pct(a, 10), "p90": _pct(a, 90)}
+
+    per_step = (stream[live] / np.maximum(steps[live], 1))
+    line = {"metric": "per-workgroup phase times of the decode, us",
+            "config": {"workload": cfg.name, "calls": calls, "workgroups_with_work": int(live[0].sum())},
+            "kernel": "pa::decode_rows_kernel",
+            "call_us_event": round(float(np.mean(call_us)), 2),
+            "decode_kernel_span_us": round(float(span.mean()), 2),
+            "dispatch_ramp": stat(ramp), "prologue": stat(pro), "first_step_data_after_prologue": stat(first),
+            "query_conversion_total": stat(qc), "segment_ends_total": stat(ends), "streaming": stat(stream),
+            "steps": {"mean": round(float(steps[live].mean()), 1), "min": int(steps[live].min()),
+                      "max": int(steps[live].max())},
+            "segments": {"mean": round(float(segs[live].mean()), 2), "max": int(segs[live].max())},
+            "us_per_streaming_step": {"mean": round(float(per_step.mean()), 3), "p10": _pct(per_step, 10),
+                                      "p90": _pct(per_step, 90)},
+            "workgroup_end": stat(end),
+            "tail_after_mean_end": round(float((span - np.array([e[l].mean() for e, l in zip(end, live)])).mean()), 2)}
+    print(json.dumps(line), flush=True)
 
 
 def run_mla(args):

@@ -30,9 +30,19 @@ def hipcc() -> str:
 EXTRA = {"pa_fp8_decode_rows.hip": ["-mllvm", "-pragma-unroll-threshold=1000000", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def build(verbose: bool = False) -> str:
+PHASES_LIB = os.path.join(PKG, "libpa_fp8_phases.so")
+
+
+def build_phases() -> str:
+    """The phase-stamp variant of the library (the same results; the decode and MLA
+    kernels also record per-workgroup phase times for bench.py --op phases);
+    writes fp8_paged_kv_amd/libpa_fp8_phases.so."""
+    return build(lib_path=PHASES_LIB, defines=["-DPA_FP8_PHASES"], objsub="_build_phases")
+
+
+def build(verbose: bool = False, lib_path: str = LIB, defines=(), objsub: str = "_build") -> str:
     """Always recompiles; writes fp8_paged_kv_amd/libpa_fp8.so."""
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, objsub)
     os.makedirs(objdir, exist_ok=True)
     base = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             # packed FP32 instructions stay off (ordinary scalar float code only)
@@ -43,7 +53,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = base + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = base + list(defines) + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
     remarks = []
     for src, pr in procs:
@@ -56,13 +66,13 @@ def build(verbose: bool = False) -> str:
         print("warning: kernels using scratch (register spills): " + ", ".join(spills))
     if verbose:
         print("\n".join(remarks))
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs,
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 PROBE_SRC = os.path.join(CSRC, "probe", "pa_probe_stream.hip")
@@ -99,3 +109,4 @@ def scratch_kernels(remarks: str) -> list:
 if __name__ == "__main__":
     print(build())
     print(build_probe())
+    print(build_phases())

@@ -31,6 +31,24 @@
 #include "pa_fp8_common.h"
 #include "pa_fp8_device.h"
 
+// Phase timing, built only into the phase-stamp variant of the library (PA_FP8_PHASES;
+// the results are those of the plain build): eight 64-bit words per workgroup --
+// 0 entry, 1 start of the main loop, 2 exit, 3 summed query conversion, 4 summed
+// segment ends (combine and stores), 5 steps, 6 segments, 7 first step's data --
+// times from s_memrealtime (100 MHz).
+#ifdef PA_FP8_PHASES
+static __device__ unsigned long long g_rows_phases[256 * 8];
+extern "C" unsigned long long* pa_fp8_phases_rows() {
+    void* p = nullptr;
+    return hipGetSymbolAddress(&p, HIP_SYMBOL(g_rows_phases)) == hipSuccess ? (unsigned long long*)p : nullptr;
+}
+#define PH_NOW() __builtin_amdgcn_s_memrealtime()
+#define PH_SET(k, v) do { if (threadIdx.x == 0) g_rows_phases[blockIdx.x * 8 + (k)] = (v); } while (0)
+#else
+#define PH_NOW() 0ull
+#define PH_SET(k, v) do { } while (0)
+#endif
+
 namespace pa {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -126,6 +144,12 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     __shared__ int s_seq[kPrefixMax];        // clamped length per batch
     __shared__ int s_units;
 
+    const unsigned long long ph_t0 = PH_NOW();
+    unsigned long long ph_q = 0, ph_end = 0, ph_t7 = 0;
+    int ph_segs = 0;
+    PH_SET(0, ph_t0);
+    PH_SET(2, ph_t0);
+    PH_SET(5, 0);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = w >> 1, p = w & 1;
@@ -446,6 +470,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         }
     };
 
+    PH_SET(1, PH_NOW());
     while (true) {
         const bool seg_start = cur.v != prev_v;
         if (seg_start) {
@@ -466,9 +491,12 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         for (int r = 0; r < NBLK; ++r) {
             if (r < cur.nvs) {
                 step_begin(r);
+                if (gs == 0) ph_t7 = PH_NOW();
                 const uint8_t* ring = s_ring[gs % NST];
                 const float* ksr = s_ks[gs % NST][w];
                 if (r == 0 && seg_start) {
+                    const unsigned long long ph_a = PH_NOW();
+                    ++ph_segs;
                     // step 1: this head's query rows -> bf16 operands of exact FP8 codes
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb) {
@@ -512,6 +540,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 #pragma unroll
                         for (int cc = 0; cc < 8; ++cc) O[rb][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
+                    ph_q += PH_NOW() - ph_a;
                 }
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
@@ -677,6 +706,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 
         // ---- end of a (batch, group) segment in this workgroup --------------------------------
         const bool seg_end = nxt.nvs == 0 || nxt.v != cur.v;
+        const unsigned long long ph_b = seg_end ? PH_NOW() : 0ull;
         if (seg_end) {
             // finished here unless some tile of the sequence lies outside this range
             const bool split = unit_mid(cur, 0) < lo || unit_mid(cur, (cur.seq + T - 1) / T - 1) >= hi;
@@ -759,6 +789,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             }
         }
 
+        if (seg_end) ph_end += PH_NOW() - ph_b;
         prev_v = cur.v;
         if (nxt.nvs == 0) break;
         cur = nxt;
@@ -767,6 +798,12 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     }
     // the workgroup retires with no load in flight (the last step waited for all of them)
     wait_vm<0>();
+    PH_SET(2, PH_NOW());
+    PH_SET(3, ph_q);
+    PH_SET(4, ph_end);
+    PH_SET(5, (unsigned long long)gs);
+    PH_SET(6, (unsigned long long)ph_segs);
+    PH_SET(7, ph_t7);
 }
 
 // Merge of the partials of split (batch, head) pairs: one workgroup per pair, 16

@@ -36,6 +36,21 @@
 #include "pa_fp8_common.h"
 #include "pa_fp8_device.h"
 
+// Phase timing, built only into the phase-stamp variant of the library (PA_FP8_PHASES;
+// the results are those of the plain build): eight 64-bit words per workgroup, times
+// from s_memrealtime (100 MHz) -- 0 entry, 1 rows and queries staged, 2 score pass
+// done, 3 tile maxima exchanged, 4 P staged, 5 P.V pass done, 6 exit.
+#ifdef PA_FP8_PHASES
+static __device__ unsigned long long g_mla_phases[4096 * 8];
+extern "C" unsigned long long* pa_fp8_phases_mla() {
+    void* p = nullptr;
+    return hipGetSymbolAddress(&p, HIP_SYMBOL(g_mla_phases)) == hipSuccess ? (unsigned long long*)p : nullptr;
+}
+#define PH_STAMP(k) do { if (threadIdx.x == 0 && blockIdx.x < 4096) g_mla_phases[blockIdx.x * 8 + (k)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define PH_STAMP(k) do { } while (0)
+#endif
+
 namespace pa {
 
 constexpr int kMlaNope = 512, kMlaRope = 64, kMlaHeads = 32;
@@ -78,6 +93,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     __shared__ float s_max[NWV][kMlaHeads], s_sum[NWV][kMlaHeads];
     __shared__ __attribute__((aligned(16))) uint8_t s_qop[2][18][64 * 16];  // Q as MFMA B operands, per lane
 
+    PH_STAMP(0);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
@@ -134,6 +150,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
         *reinterpret_cast<i32x4*>(&s_qop[hh][ks][16 * lane]) = *reinterpret_cast<const i32x4*>(src);
     }
     __syncthreads();
+    PH_STAMP(1);
     auto qop = [&](int hh, int ks) { return *reinterpret_cast<const bf16x8*>(&s_qop[hh][ks][16 * lane]); };
 
     // ---- scores of this wave's rows: S^T (rows x heads), log2 units ------------------------
@@ -196,7 +213,9 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
         const float m = wave_max_over_groups(rmax[hh]);
         if (lg == 0) s_max[w][16 * hh + lr] = m;
     }
+    PH_STAMP(2);
     __syncthreads();
+    PH_STAMP(3);
 
     // ---- tile max, P = exp2(S - m) in BF16 to LDS, unquantised sums -------------------------
     float mt[2];
@@ -223,6 +242,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     }
     __syncthreads();
 
+    PH_STAMP(4);
     // ---- P.V for channels [CPW w, CPW w + CPW): O[head][channel] -------------------------
     f32x4 O[2][CL];
 #pragma unroll
@@ -290,6 +310,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
         }
     }
 
+    PH_STAMP(5);
     // ---- partial of this tile: O (relative to the tile max), m, l --------------------------
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -313,6 +334,7 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
             a.part_ml[slot * 2 + 1] = l;
         }
     }
+    PH_STAMP(6);
 }
 
 // Online merge of the tile partials of every (query token, head), in tile order;
