@@ -633,7 +633,7 @@ def run_phases(args):
     for i in range(args.warmup):
         binding.decode_inputs(sets[i % len(sets)], out=out, workspace=ws)
     torch.cuda.synchronize()
-    buf = np.zeros(256 * 8, dtype=np.uint64)
+    buf = np.zeros(256 * 16, dtype=np.uint64)
     rows = []
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     call_us = []
@@ -644,8 +644,8 @@ def run_phases(args):
         torch.cuda.synchronize()
         call_us.append(e0.elapsed_time(e1) * 1e3)
         hip.hipMemcpy(buf.ctypes.data, ptr, buf.nbytes, 2)
-        rows.append(buf.reshape(256, 8).astype(np.int64).copy())
-    st = np.stack(rows)                                        # [calls, 256, 8]
+        rows.append(buf.reshape(256, 16).astype(np.int64).copy())
+    st = np.stack(rows)                                        # [calls, 256, 16]
     live = st[:, :, 5] > 0                                     # workgroups that had work
     t0 = st[:, :, 0].min(axis=1, keepdims=True)
     ramp = (st[:, :, 0] - t0) * us
@@ -668,7 +668,13 @@ def run_phases(args):
             "kernel": "pa::decode_rows_kernel",
             "call_us_event": round(float(np.mean(call_us)), 2),
             "decode_kernel_span_us": round(float(span.mean()), 2),
-            "dispatch_ramp": stat(ramp), "prologue": stat(pro), "first_step_data_after_prologue": stat(first),
+            "dispatch_ramp": stat(ramp), "prologue": stat(pro),
+            "prologue_parts": {"lengths_staged": stat((st[:, :, 8] - st[:, :, 0]) * us),
+                               "cost_prefix": stat((st[:, :, 9] - st[:, :, 8]) * us),
+                               "first_unit_found": stat((st[:, :, 10] - st[:, :, 9]) * us),
+                               "table_entries_arrived": stat((st[:, :, 11] - st[:, :, 10]) * us),
+                               "first_loads_issued": stat((st[:, :, 1] - st[:, :, 11]) * us)},
+            "first_step_data_after_prologue": stat(first),
             "query_conversion_total": stat(qc), "segment_ends_total": stat(ends), "streaming": stat(stream),
             "steps": {"mean": round(float(steps[live].mean()), 1), "min": int(steps[live].min()),
                       "max": int(steps[live].max())},

@@ -32,18 +32,19 @@
 #include "pa_fp8_device.h"
 
 // Phase timing, built only into the phase-stamp variant of the library (PA_FP8_PHASES;
-// the results are those of the plain build): eight 64-bit words per workgroup --
+// the results are those of the plain build): sixteen 64-bit words per workgroup --
 // 0 entry, 1 start of the main loop, 2 exit, 3 summed query conversion, 4 summed
-// segment ends (combine and stores), 5 steps, 6 segments, 7 first step's data --
-// times from s_memrealtime (100 MHz).
+// segment ends (combine and stores), 5 steps, 6 segments, 7 first step's data,
+// 8 lengths staged, 9 cost prefix done, 10 first unit found, 11 its table entries
+// arrived -- times from s_memrealtime (100 MHz).
 #ifdef PA_FP8_PHASES
-static __device__ unsigned long long g_rows_phases[256 * 8];
+static __device__ unsigned long long g_rows_phases[256 * 16];
 extern "C" unsigned long long* pa_fp8_phases_rows() {
     void* p = nullptr;
     return hipGetSymbolAddress(&p, HIP_SYMBOL(g_rows_phases)) == hipSuccess ? (unsigned long long*)p : nullptr;
 }
 #define PH_NOW() __builtin_amdgcn_s_memrealtime()
-#define PH_SET(k, v) do { if (threadIdx.x == 0) g_rows_phases[blockIdx.x * 8 + (k)] = (v); } while (0)
+#define PH_SET(k, v) do { if (threadIdx.x == 0) g_rows_phases[blockIdx.x * 16 + (k)] = (v); } while (0)
 #else
 #define PH_NOW() 0ull
 #define PH_SET(k, v) do { } while (0)
@@ -164,6 +165,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         s_seq[b] = s < 0 ? 0 : (s > a.capacity ? a.capacity : s);
     }
     __syncthreads();
+    PH_SET(8, PH_NOW());
     if (w == 0) {
         const int strip = (BV + 63) / 64;
         const int v0 = lane * strip, v1 = min(v0 + strip, BV);
@@ -201,6 +203,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         if (lane == 0) s_units = units;
     }
     __syncthreads();
+    PH_SET(9, PH_NOW());
     const int64_t C = lds_uniform(&s_pref[BV]);
     const int U = lds_uniform(&s_units);
     const int Geff = min((int)gridDim.x, U);
@@ -333,6 +336,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             if (threadIdx.x == 0) a.part_tag[2 * g] = a.part_tag[2 * g + 1] = -1;
             return;
         }
+        PH_SET(10, PH_NOW());
         cur = make_unit(v, b, h0, seq, t, true);   // its table loads overlap the Q staging below
     }
     const int first_v = cur.v;               // the range's first (batch, group)
@@ -437,6 +441,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     int nseg_issued = 1;                     // sequences staged so far (segment i uses buffer i & 1)
     int vs_buf = 1;
     finish_ids(cur);
+    PH_SET(11, PH_NOW());
     issue(cur, 0, 0);
     issue(cur, 1, 1);
     nxt = next_unit(cur);
