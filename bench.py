@@ -365,7 +365,7 @@ def measure_mla(kv_split, steps, warmup, rotate):
         sets = [synth.mla_kv_split(st) for st in sets]
     run_one = binding.mla_decode_kv_split_inputs if kv_split else binding.mla_decode_inputs
     out = torch.empty((cfg.B * cfg.s1 * cfg.nq, 512), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(binding.mla_workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
+    ws = torch.zeros(binding.mla_workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
                      device="cuda")
 
     def call(i, stream):
@@ -593,7 +593,7 @@ def run_phases(args):
         sets = [first] + [synth.make_mla_inputs(cfg, device="cuda", seed=1000 + 17 * i + cfg.seed, seq_lens=seqs)
                           for i in range(1, max(1, args.rotate))]
         out = torch.empty((cfg.B * cfg.nq, 512), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(binding.mla_workspace_size(cfg.B, 1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
+        ws = torch.zeros(binding.mla_workspace_size(cfg.B, 1, cfg.nq, cfg.topk, cfg.s2_tile), dtype=torch.uint8,
                          device="cuda")
         grid = cfg.B * cfg.s1 * ((cfg.topk + cfg.s2_tile - 1) // cfg.s2_tile) * (cfg.nq // 32)
         names = ["rows and queries staged", "score pass", "wait for the tile maxima", "softmax, P to LDS",

@@ -274,7 +274,9 @@ def test_prefill_causal_parity(B, oracle_mod, s1, nq, nkv, s2_tile, seqs):
     ref = _rows_ref(oracle_mod, inp)
     for ns in (0, 2):
         got = _run(B, inp, ns, f"prefill s1={s1}")
-        compare(got.reshape(-1, 128), ref, f"prefill causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile} splits={ns}")
+        # measured: at most 7 ulps (s1 = 128, one KV head)
+        compare(got.reshape(-1, 128), ref, f"prefill causal s1={s1} nq={nq} nkv={nkv} tile={s2_tile} splits={ns}",
+                max_ulps=16)
         rows = got.reshape(len(seqs), s1, nq, 128)
         for bi, sq in enumerate(seqs):          # positions that see no token are zero rows
             nz = max(0, s1 - sq)

@@ -61,19 +61,26 @@ def _decode(B, dev, tag, num_splits=0):
     return gpu_out_float(out)
 
 
+# Regression gates on the largest distance, in bf16 ulps, from the oracle's own bf16
+# output (ulps of max(|ref|, 1/16)); about twice the level measured when they were set
+# (config 1: 19, where a few outputs near zero sum outliers x20; config 2: 1; config 3
+# and its causal variant: 4; the page shapes: 0; MLA: 1).
+MAX_ULPS = {1: 40, 2: 4, 3: 8}
+
+
 @pytest.mark.parametrize("cfg_id", [1, 2, 3])
 def test_full_size_every_element(B, cfg_id):
     dev, _, ref = _inputs(cfg_id)
     cfg = synth.CONFIGS[cfg_id]
     got = _decode(B, dev, f"config{cfg_id} full").reshape(cfg.B * cfg.s1 * cfg.nq, cfg.D)
     compare(got, {"out": ref["out"].reshape(got.shape), "out_bf16": ref["out_bf16"].reshape(got.shape)},
-            f"config{cfg_id} full, whole-row path")
+            f"config{cfg_id} full, whole-row path", max_ulps=MAX_ULPS[cfg_id])
 
 
 def test_full_size_config3_causal_every_element(B):
     dev, _, ref = _inputs(3, causal=True)
     got = _decode(B, dev, "config3 causal full")
-    compare(got, ref, "config3 causal full")
+    compare(got, ref, "config3 causal full", max_ulps=MAX_ULPS[3])
 
 
 def test_full_size_config1_dumps_bit_exact(B):
@@ -88,7 +95,7 @@ def test_full_size_config1_dumps_bit_exact(B):
     torch.cuda.synchronize()
     assert np.array_equal(rows.cpu().numpy(), ref["rows"])
     assert np.array_equal(q8.cpu().numpy(), ref["q8"])
-    compare(gpu_out_float(out), ref, "config1 full debug")
+    compare(gpu_out_float(out), ref, "config1 full debug", max_ulps=MAX_ULPS[1])
 
 
 @pytest.mark.parametrize("num_splits", [1, 4])
@@ -98,7 +105,7 @@ def test_full_size_config1_per_head_path(B, num_splits):
     dev, _, ref = _inputs(1)
     cfg = synth.CONFIGS[1]
     got = _decode(B, dev, "config1 full per-head", num_splits)
-    compare(got, ref, f"config1 full per-head splits={num_splits}")
+    compare(got, ref, f"config1 full per-head splits={num_splits}", max_ulps=MAX_ULPS[1])
     print(f"[gpu] config1 full debug dumps, per-head path, splits={num_splits}", flush=True)
     _, rows, q8 = B.decode_debug(dev["q"], dev["q_scale"], dev["k_cache"], dev["k_scale"], dev["v_cache"],
                                  dev["v_scale"], dev["block_table"], dev["kv_act_seqs"], dev["softmax_scale"],
@@ -129,7 +136,7 @@ def test_page_test_shapes(B, oracle_mod, shape, s2_tile):
         print(f"[gpu] page shape {shape} s2_tile={s2_tile} splits={ns}", flush=True)
         out = B.decode_inputs(d, num_splits=ns)
         torch.cuda.synchronize()
-        compare(gpu_out_float(out), ref, f"page shape {shape} s2_tile={s2_tile} splits={ns}")
+        compare(gpu_out_float(out), ref, f"page shape {shape} s2_tile={s2_tile} splits={ns}", max_ulps=2)
 
 
 @pytest.fixture(scope="module")
@@ -146,7 +153,7 @@ def test_full_size_mla_every_element(B, mla_full):
     print("[gpu] mla config4 full, packed rows", flush=True)
     out = B.mla_decode_inputs(to_device(inp))
     torch.cuda.synchronize()
-    compare(gpu_out_float(out), ref, "mla config4 full, packed rows")
+    compare(gpu_out_float(out), ref, "mla config4 full, packed rows", max_ulps=4)
 
 
 def test_full_size_mla_kv_split_every_element(B, mla_full):
@@ -154,4 +161,4 @@ def test_full_size_mla_kv_split_every_element(B, mla_full):
     print("[gpu] mla config4 full, kv_split", flush=True)
     out = B.mla_decode_kv_split_inputs(to_device(synth.mla_kv_split(inp)))
     torch.cuda.synchronize()
-    compare(gpu_out_float(out), ref, "mla config4 full, kv_split")
+    compare(gpu_out_float(out), ref, "mla config4 full, kv_split", max_ulps=4)
