@@ -98,6 +98,19 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
 
 __device__ __forceinline__ int lds_uniform(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
 
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts by 1, 2, 4 and 8 (a lane
+// with no source in its 16-lane row adds 0), then lane 15 of rows 0 and 2 into rows 1
+// and 3, and lane 31 into rows 2 and 3 (DPP row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+    return x;
+}
+
 // floor(x / d) for 0 <= x and x + d < 2^22, given inv = 1.0f / d (IEEE): (x + 0.5) / d lies at
 // least 0.5 / d from an integer and the two roundings move it by less than that.
 __device__ __forceinline__ int small_div(int x, float inv) { return (int)(((float)x + 0.5f) * inv); }
@@ -181,12 +194,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                 ++bb;
             }
         }
-        int incl = cost;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int x = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += x;
-        }
+        const int incl = wave_incl_scan(cost);
         int run = incl - cost;
         for (int v = v0, bb = bs0, gg = gs0; v < v1; ++v) {
             s_pref[v] = run;
@@ -198,9 +206,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             }
         }
         if (lane == 63) s_pref[BV] = incl;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) units += __shfl_xor(units, o, 64);
-        if (lane == 0) s_units = units;
+        units = wave_incl_scan(units);
+        if (lane == 63) s_units = units;
     }
     __syncthreads();
     PH_SET(9, PH_NOW());
