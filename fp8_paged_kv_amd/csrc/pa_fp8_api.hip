@@ -71,7 +71,7 @@ int plan_splits(int B, int nkv, int row_blocks, int max_tiles, int requested) {
     const int64_t units = (int64_t)B * nkv * row_blocks;
     const int64_t target = 2048;                  // launched workgroups to aim for
     int64_t s = (target + units - 1) / units;
-    if (s <= 1) return 1;
+    if (s <= 1 || units >= 1024) return 1;        // four or more workgroups per CU already
     s = (s + 7) / 8 * 8;
     if (s > max_tiles) s = max_tiles;
     return (int)s;
