@@ -315,6 +315,17 @@ def causal_flops(cfg, seqs):
     return 4 * cfg.D * G * cfg.nkv * tok
 
 
+def whole_row_path(cfg):
+    """Whether the library runs this shape on its whole-row path (the header's rule for
+    num_splits = 0): at most 32 query rows per KV head, or more in blocks of 32 with
+    s2_tile up to 512; at most 1024 (batch, KV-head group, row block) units."""
+    rows = cfg.s1 * cfg.nq // cfg.nkv
+    rbk = 1 if rows <= 32 else (rows + 31) // 32
+    hg = 2 if cfg.nkv % 2 == 0 else 1
+    tile_ok = cfg.s2_tile in (128, 256, 512) or (cfg.s2_tile == 1024 and rows <= 16)
+    return tile_ok and cfg.B * rbk * (cfg.nkv // hg) <= 1024
+
+
 def measure_gqa(cfg_id, causal, steps, warmup, rotate, cfg=None):
     """Event-timed decode calls on one GQA workload (rotating input sets):
     algorithmic bytes, us per call and the HBM roofline fraction (the bf16 MFMA one
@@ -335,14 +346,14 @@ def measure_gqa(cfg_id, causal, steps, warmup, rotate, cfg=None):
     torch.cuda.empty_cache()
     gbs = nbytes / (region * 1e-3) / 1e9
     rows = cfg.s1 * cfg.nq // cfg.nkv
-    whole_row = rows <= 32
     entry = {"workload": cfg.name + ("-causal" if causal else ""), "algorithmic_bytes_per_call": nbytes,
              "us_per_call": round(region * 1e3, 2), "median_us": round(ev[len(ev) // 2] * 1e3, 2),
              "calls_per_s": round(1e3 / region, 1),
              "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gbs / HBM_PEAK_GBS, 4)},
-             "kernel": ("pa::decode_rows_kernel + pa::merge_rows_kernel" if whole_row else "pa::decode_kernel")}
-    if not whole_row:
+             "kernel": ("pa::decode_rows_kernel + pa::merge_rows_kernel" if whole_row_path(cfg)
+                        else "pa::decode_kernel")}
+    if rows > 32:
         flops = causal_flops(cfg, seqs) if causal else 4 * cfg.D * cfg.s1 * cfg.nq * sum(seqs)
         tf = flops / (region * 1e-3) / 1e12
         entry["flop_per_call"] = flops

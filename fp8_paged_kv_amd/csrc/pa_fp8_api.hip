@@ -143,19 +143,21 @@ struct WorkspaceLayout {
 };
 
 // Per-head path with splits: [U int32 counters | pad][U*nsplit*R*2 | pad][U*nsplit*R*128], U = B*nkv*row blocks
-// Whole-row path:             [B*nkv int32, untouched | pad][B*nkv+2 int32 partition | pad]
+// Whole-row path:             [U int32, untouched | pad][U+2 int32 partition | pad]
 //                             [256*2 int32 slot tags | pad][256*2*HG*R*2 | pad][256*2*HG*R*128]
-// with two partial slots per workgroup (its first and last segment, the only ones that can
-// be split), HG KV heads per workgroup and R query rows per KV head padded to 16.
-// The whole-row path never writes the first B*nkv words, so the per-head path's arrival
-// counters stay zero when one workspace serves calls of both paths.
+// with U = B*nkv*row blocks, two partial slots per workgroup (its first and last segment,
+// the only ones that can be split), HG KV heads per workgroup and R query rows per block
+// (all of a KV head's rows padded to 16, or 32).  The whole-row path never writes the
+// first U words, so the per-head path's arrival counters stay zero when one workspace
+// serves calls of both paths.
 WorkspaceLayout layout_for(int B, int s1, int nq, int nkv, int nsplit, bool rows) {
     WorkspaceLayout l = {0, 0, 0, 0, 0};
     if (rows) {
-        const size_t units = (size_t)B * nkv, R = (size_t)rows_pad(s1, nq, nkv);
+        const int rbk = pa::rows_row_blocks(s1 * (nq / nkv));
+        const size_t units = (size_t)B * nkv * rbk, R = (size_t)(rbk > 1 ? 32 : rows_pad(s1, nq, nkv));
         const size_t slots = (size_t)pa::kRowsMaxGrid * 2 * pa::rows_group(nkv);
         l.meta = align256(units * sizeof(int32_t));
-        l.tags = l.meta + align256(((size_t)B * nkv + 2) * sizeof(int32_t));
+        l.tags = l.meta + align256((units + 2) * sizeof(int32_t));
         l.part_ml = l.tags + align256((size_t)pa::kRowsMaxGrid * 2 * sizeof(int32_t));
         l.part_o = l.part_ml + align256(slots * R * 2 * sizeof(float));
         l.total = l.part_o + slots * R * pa::kHeadDim * sizeof(float);
@@ -190,7 +192,7 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     const int capacity = max_blocks * block_size;
     const int max_tiles = (capacity + s2_tile - 1) / s2_tile;
     const bool rows = use_rows_path(B, s1, nq, nkv, s2_tile, num_splits);
-    const int rblocks = rows ? 1 : head_row_blocks(s1, nq, nkv);
+    const int rblocks = rows ? pa::rows_row_blocks(s1 * (nq / nkv)) : head_row_blocks(s1, nq, nkv);
     const int nsplit = rows ? 1 : plan_splits(B, nkv, rblocks, max_tiles, num_splits);
     const int tps = (max_tiles + nsplit - 1) / nsplit;
     const WorkspaceLayout lay = layout_for(B, s1, nq, nkv, nsplit, rows);
@@ -241,7 +243,7 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
     p.nsplit = nsplit;
     p.nsplit_pad = nsplit_pad;
     p.tiles_per_split = tps;
-    p.row_block = rows ? rows_pad(s1, nq, nkv) : head_row_block(s1, nq, nkv);
+    p.row_block = rows ? (rblocks > 1 ? 32 : rows_pad(s1, nq, nkv)) : head_row_block(s1, nq, nkv);
     p.row_blocks = rblocks;
     p.softmax_scale = softmax_scale;
     p.causal = causal ? 1 : 0;

@@ -31,7 +31,8 @@ struct DecodeParams {
     int B, s1, nq, nkv, G, rows;
     int s2_tile, max_blocks, num_blocks, capacity;
     int nsplit, nsplit_pad, tiles_per_split;
-    int row_block, row_blocks;  // per-head path: query rows per workgroup (16..64) and blocks of them per KV head
+    int row_block, row_blocks;  // query rows per block (padded) and blocks per KV head: per-head path
+                                // 16..64 per workgroup; whole-row path all rows (<= 32) or blocks of 32
     int causal;                 // position s of s1 sees the first seq - s1 + 1 + s tokens
     float softmax_scale;
 };
@@ -86,6 +87,7 @@ int grid_size(const DecodeParams& p);
 bool rows_path_supported(int nkv, int s2_tile, int rows, int s1, int nq, int B);
 constexpr int kRowsMaxGrid = 256;   // whole-row path: at most one workgroup per CU, at most 256
 int rows_group(int nkv);            // KV heads per whole-row workgroup
+int rows_row_blocks(int rows);      // query-row blocks per KV head on the whole-row path
 hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t stream, bool debug);
 hipError_t launch_fill_rows(const DecodeParams& p, hipStream_t stream);
 

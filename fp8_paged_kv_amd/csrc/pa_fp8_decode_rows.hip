@@ -168,13 +168,17 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = w >> 1, p = w & 1;
     const int lr = lane & 15, lg = lane >> 4;
-    const int B = a.B, NG = a.nkv / HG, BV = B * NG;
+    // A unit of work is (batch, head group, row block): a KV head's query rows come in
+    // blocks of 32 when there are more than 32 of them (a prefill chunk), each block a
+    // sequence of its own here ("virtual batch" bv = b RBK + block), all reading the same
+    // K and V; with at most 32 rows, RBK = 1 and bv = b.
+    const int RBK = a.row_blocks, B = a.B * RBK, NG = a.nkv / HG, BV = B * NG;
     const int nkv = a.nkv;
-    const float inv_ng = 1.0f / NG, inv_g = 1.0f / a.G;
+    const float inv_ng = 1.0f / NG, inv_g = 1.0f / a.G, inv_rbk = 1.0f / RBK;
 
     // ---- lengths, cost prefix and unit count ------------------------------------------------
     for (int b = threadIdx.x; b < B; b += NW * 64) {
-        const int s = a.seqs[b];
+        const int s = a.seqs[RBK == 1 ? b : small_div(b, inv_rbk)];
         s_seq[b] = s < 0 ? 0 : (s > a.capacity ? a.capacity : s);
     }
     __syncthreads();
@@ -226,10 +230,25 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         if (threadIdx.x == 0) a.rows_meta[BV + 1] = Geff;
     }
     // rows of empty sequences are zero: workgroup g clears batches g, g + grid, ...
-    for (int b = g; b < B; b += gridDim.x) {
-        if (lds_uniform(&s_seq[b]) != 0) continue;
+    for (int b = g; b < a.B; b += gridDim.x) {
+        if (lds_uniform(&s_seq[b * RBK]) != 0) continue;
         for (int e = threadIdx.x; e < a.s1 * a.nq * kHeadDim; e += NW * 64)
             a.out[(int64_t)b * a.s1 * a.nq * kHeadDim + e] = 0;
+        if (DBG && a.dbg_q8) {
+            // the query codes of step 1 for the dump, which no unit of this batch computes
+            for (int e = threadIdx.x; e < a.s1 * a.nq * (kHeadDim / 16); e += NW * 64) {
+                const int64_t qrow = (int64_t)b * a.s1 * a.nq + e / (kHeadDim / 16);
+                const int d0 = 16 * (e % (kHeadDim / 16));
+                const i32x4 v0 = *reinterpret_cast<const i32x4*>(a.q + qrow * kHeadDim + d0);
+                const i32x4 v1 = *reinterpret_cast<const i32x4*>(a.q + qrow * kHeadDim + d0 + 8);
+                const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
+                                         (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
+                uint32_t wds[4];
+                quantise_q16(raw, q_recip(a.q_scale[qrow]), wds);
+                *reinterpret_cast<i32x4*>(a.dbg_q8 + qrow * kHeadDim + d0) =
+                    i32x4{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3]};
+            }
+        }
     }
     if (g >= Geff) return;
 
@@ -240,7 +259,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     // A unit carries its sequence's batch, head group and length, so that stepping to the
     // next tile of the same sequence divides nothing.
     struct Unit {
-        int v, b, h0, t, seq;
+        int v, b, h0, t, seq;                // b: the virtual batch
+        int br, rk;                          // its batch and row block
         int nvs;                             // valid blocks (steps per pass); 0 = no unit
         int ids;                             // lane i < NBLK: physical block of block i of the tile
         int raw[NBLK];                       // the table entries as loaded (scalar), until finish_ids
@@ -257,12 +277,14 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         u.h0 = ok ? h0 : 0;
         u.t = t;
         u.seq = ok ? seq : 0;
+        u.br = RBK == 1 ? u.b : small_div(u.b, inv_rbk);
+        u.rk = u.b - u.br * RBK;
         u.nvs = ok ? min(NBLK, nblocks(u.seq) - t * NBLK) : 0;
         // the scalar table loads are only issued here; finish_ids, called when the unit's
         // first step is about to be issued, waits for them (they then have long arrived)
 #pragma unroll
         for (int i = 0; i < NBLK; ++i)
-            u.raw[i] = ok ? ld_uniform(a.block_table, (int64_t)u.b * a.max_blocks + min(t * NBLK + i, a.max_blocks - 1)) : 0;
+            u.raw[i] = ok ? ld_uniform(a.block_table, (int64_t)u.br * a.max_blocks + min(t * NBLK + i, a.max_blocks - 1)) : 0;
         u.ids = 0;
         return u;
     };
@@ -391,42 +413,35 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
         dma4(ksb, ksoff, (lds_ptr)(&s_ks[st][w][0]));
     };
 
-    // The QNW loads of this wave that stage the query rows and q_scale of heads
-    // h0 .. h0+HG-1 of batch b (staged row hl * rows + rr) and their v_scale.  Staged
-    // row sr = hs * rows + s * G + gq is query row b s1 nq + s nq + (h0 + hs) G + gq; the
-    // part that depends on neither b nor h0 is a per-lane constant (-1: padding row).
-    const int rows = a.rows;
-    int qoff[QNW];
-    {
+    // The QNW loads of this wave that stage the query rows and q_scale of the unit's heads
+    // h0 .. h0+HG-1 and their v_scale.  Staged row sr = hs * qstride + rr (rr < the block's
+    // rows) is query row ra = 32 rk + rr of head h0 + hs: b s1 nq + s nq + (h0 + hs) G + gq
+    // with (s, gq) = divmod(ra, G).  Padding rows stage the batch's first row (unused).
+    const int qstride = RBK == 1 ? a.rows : 32;   // staged rows per head
+    const float inv_qstride = 1.0f / qstride;
+    auto issue_q = [&](const Unit& u, int buf) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const float inv_rows = 1.0f / rows;
+        const int rows_u = min(32, a.rows - 32 * u.rk);
         auto off_of = [&](int sr) {
-            const int hs = small_div(sr, inv_rows), rr = sr - hs * rows;
-            const int s = small_div(rr, inv_g), gq = rr - s * a.G;
-            return sr < HG * rows ? s * a.nq + hs * a.G + gq : -1;
+            const int hs = small_div(sr, inv_qstride), rr = sr - hs * qstride;
+            const int ra = 32 * u.rk + rr;
+            const int s = small_div(ra, inv_g), gq = ra - s * a.G;
+            return (sr < HG * qstride && rr < rows_u) ? s * a.nq + hs * a.G + gq : -1;
         };
+        const int qrow0 = u.br * a.s1 * a.nq;                  // first query row of the batch
+        const int qrowh = qrow0 + u.h0 * a.G;
 #pragma unroll
         for (int n = 0; n < QNW; ++n) {
             const int j = w + n * NW;
-            qoff[n] = j < QI ? off_of(4 * j + (ln >> 4)) : (j == QI ? off_of(ln) : -1);
-        }
-    }
-    auto issue_q = [&](int b, int h0, int buf) {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int qrow0 = b * a.s1 * a.nq;                     // first query row of batch b
-        const int qrowh = qrow0 + h0 * a.G;
-#pragma unroll
-        for (int n = 0; n < QNW; ++n) {
-            const int j = w + n * NW;
-            const int row = qoff[n] >= 0 ? qrowh + qoff[n] : qrow0;
+            const int off = j < QI ? off_of(4 * j + (ln >> 4)) : (j == QI ? off_of(ln) : -1);
+            const int row = off >= 0 ? qrowh + off : qrow0;
             if (j < QI) {
                 dma16(a.q, (uint32_t)(row * 256 + 16 * (ln & 15)), (lds_ptr)(&s_q[buf][j * 1024]));
             } else if (j == QI) {
                 dma4(a.q_scale, (uint32_t)(row * 4), (lds_ptr)(&s_qs[buf][0]));
             } else if (j == QI + 1) {
-                const uint32_t vb = (uint32_t)((b * nkv + h0) * kHeadDim * 4);
+                const uint32_t vb = (uint32_t)((u.br * nkv + u.h0) * kHeadDim * 4);
                 dma16(a.v_scale, vb + (16 * ln < HG * kHeadDim * 4 ? 16 * ln : 0), (lds_ptr)(&s_vs[buf][0]));
             } else {
                 dma4(a.q_scale, (uint32_t)(qrow0 * 4), (lds_ptr)(&s_qpad[w][0]));
@@ -443,7 +458,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     f32x4 O[NRB][8];
 
     // prologue: Q of the first sequence, then the first AHEAD steps (a unit has >= 2)
-    issue_q(cur.b, cur.h0, 0);
+    issue_q(cur, 0);
     int last_q_step = 0;                     // step whose loads followed the latest Q staging
     int nseg_issued = 1;                     // sequences staged so far (segment i uses buffer i & 1)
     int vs_buf = 1;
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                 nxt_ready = true;
             }
             if (k == 0 && nxt.nvs > 0 && nxt.v != cur.v) {
-                issue_q(nxt.b, nxt.h0, nseg_issued & 1);
+                issue_q(nxt, nseg_issued & 1);
                 ++nseg_issued;
                 last_q_step = gs + AHEAD;
             }
@@ -485,6 +500,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     PH_SET(1, PH_NOW());
     while (true) {
         const bool seg_start = cur.v != prev_v;
+        const int cur_rows = min(32, a.rows - 32 * cur.rk);   // query rows of this unit's block
         if (seg_start) {
             vs_buf ^= 1;
         }
@@ -516,10 +532,11 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                         uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                         qcoef[rb] = 0.f;
                         // causal decode: position s of s1 attends to the first seq - s1 + 1 + s tokens
-                        lim[rb] = cur.seq - (a.causal ? a.s1 - 1 - (rr < rows ? small_div(rr, inv_g) : a.s1 - 1) : 0);
+                        const int ra = 32 * cur.rk + rr;           // the row among the head's s1 G
+                        lim[rb] = cur.seq - (a.causal ? a.s1 - 1 - (rr < cur_rows ? small_div(ra, inv_g) : a.s1 - 1) : 0);
                         mlim = cur.seq - (a.causal ? a.s1 - 1 : 0);
-                        if (rr < rows) {
-                            const int sr = hl * rows + rr;
+                        if (rr < cur_rows) {
+                            const int sr = hl * qstride + rr;
                             const float qs = s_qs[vs_buf][sr];
                             qcoef[rb] = qs * a.softmax_scale * kLog2e;
                             const QRecip qd = q_recip(qs);
@@ -533,8 +550,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                                 quantise_q16(raw, qd, &wds[hlf * 4]);
                             }
                             if (DBG && a.dbg_q8 && p == 0) {
-                                const int s = small_div(rr, inv_g), gq = rr - s * a.G;
-                                const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
+                                const int s = small_div(ra, inv_g), gq = ra - s * a.G;
+                                const int64_t qrow = ((int64_t)cur.br * a.s1 + s) * a.nq + h * a.G + gq;
                                 uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;
 #pragma unroll
                                 for (int hlf = 0; hlf < 2; ++hlf)
@@ -564,7 +581,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 #pragma unroll
                         for (int k = 0; k < 2; ++k)
                             if (p0 + 16 * k + lr < cur.seq)
-                                a.dbg_rows[(int64_t)cur.b * a.capacity + p0 + 16 * k + lr] = (int32_t)(s0 + 16 * k + lr);
+                                a.dbg_rows[(int64_t)cur.br * a.capacity + p0 + 16 * k + lr] = (int32_t)(s0 + 16 * k + lr);
                     }
                     const f32x4 k0 = *reinterpret_cast<const f32x4*>(&ksr[32 * cc + 4 * lg]);
                     const f32x4 k1 = *reinterpret_cast<const f32x4*>(&ksr[32 * cc + 16 + 4 * lg]);
@@ -765,9 +782,10 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                     for (int i = 0; i < 4; ++i) {
                         const int rr = rb * 16 + 4 * lg + i;
                         const float Lr = __shfl(Lw, 4 * lg + i, 64);
-                        if (rr >= rows) continue;
-                        const int s = small_div(rr, inv_g), gq = rr - s * a.G;
-                        const int64_t qrow = ((int64_t)cur.b * a.s1 + s) * a.nq + h * a.G + gq;
+                        if (rr >= cur_rows) continue;
+                        const int ra = 32 * cur.rk + rr;
+                        const int s = small_div(ra, inv_g), gq = ra - s * a.G;
+                        const int64_t qrow = ((int64_t)cur.br * a.s1 + s) * a.nq + h * a.G + gq;
                         if (!split) {
                             // step 10: out = O * v_scale / L' (L' = 448 L), bf16
                             const float inv = Lr > 0.f ? 1.f / Lr : 0.f;     // no token at all (causal): zeros
@@ -827,9 +845,10 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
 // which of a workgroup's two slots holds that segment.
 template <int NBLK, int HG>
 __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) {
-    const int NG = a.nkv / HG, BV = a.B * NG;
-    const int bh = blockIdx.x, b = bh / a.nkv, h = bh - b * a.nkv;
-    const int v = b * NG + h / HG, hl = h - (h / HG) * HG;
+    const int RBK = a.row_blocks, NG = a.nkv / HG, BV = a.B * RBK * NG;
+    const int bh = blockIdx.x, bv = bh / a.nkv, h = bh - bv * a.nkv;   // (virtual batch, head)
+    const int b = bv / RBK, rk = bv - b * RBK;
+    const int v = bv * NG + h / HG, hl = h - (h / HG) * HG;
     const int* meta = a.rows_meta;
     // independent loads first
     const int64_t C = meta[BV];
@@ -850,7 +869,7 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
     };
     auto owner = [&](int64_t x) -> int { return floor_div64((x + 1) * Geff - 1, C); };
     const int g0 = owner(mid_of(0)), g1 = owner(mid_of(nt - 1));
-    if (g0 == g1 || rr >= a.rows) return;      // finished in place by the decode kernel
+    if (g0 == g1 || rr >= min(32, a.rows - 32 * rk)) return;   // finished in place by the decode kernel
     const int n = g1 - g0 + 1;                 // <= the decode grid (<= 256)
     float Mx = -INFINITY, L = 0.f;
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
@@ -888,7 +907,8 @@ __global__ __launch_bounds__(512) void merge_rows_kernel(DecodeParams a, int R) 
             Mx = mn;
         }
     }
-    const int sq = small_div(rr, 1.0f / a.G), gq = rr - sq * a.G;
+    const int ra = 32 * rk + rr;                 // the row among the head's s1 G
+    const int sq = small_div(ra, 1.0f / a.G), gq = ra - sq * a.G;
     const int64_t qrow = ((int64_t)b * a.s1 + sq) * a.nq + h * a.G + gq;
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint32_t pk[4];
@@ -915,13 +935,14 @@ static hipError_t launch_rows_t(const DecodeParams& p, int grid, hipStream_t st,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // one workgroup per (batch, head); 16 threads per query row
-    hipLaunchKernelGGL((merge_rows_kernel<NBLK, HG>), dim3(p.B * p.nkv), dim3(NRB * 256), 0, st, p, NRB * 16);
+    hipLaunchKernelGGL((merge_rows_kernel<NBLK, HG>), dim3(p.B * p.row_blocks * p.nkv), dim3(NRB * 256), 0, st, p,
+                       NRB * 16);
     return hipGetLastError();
 }
 
 template <int HG>
 static hipError_t launch_rows_hg(const DecodeParams& p, int grid, hipStream_t st, bool dbg) {
-    const bool two = p.rows > 16;
+    const bool two = p.row_block > 16;
     switch (p.s2_tile) {
         case 128: return two ? launch_rows_t<2, 1, HG>(p, grid, st, dbg) : launch_rows_t<1, 1, HG>(p, grid, st, dbg);
         case 256: return two ? launch_rows_t<2, 2, HG>(p, grid, st, dbg) : launch_rows_t<1, 2, HG>(p, grid, st, dbg);
@@ -930,13 +951,20 @@ static hipError_t launch_rows_hg(const DecodeParams& p, int grid, hipStream_t st
     }
 }
 
+// Row blocks per KV head on the whole-row path: one for up to 32 query rows, else
+// blocks of 32.
+int rows_row_blocks(int rows) { return rows <= 32 ? 1 : (rows + 31) / 32; }
+
 // Shapes of the whole-row path: any nkv; s2_tile 128-1024; up to 32 query rows per
-// KV head (16 for s2_tile 1024); at most kPrefixMax (batch, head group) pairs.
+// KV head (16 for s2_tile 1024), or more in blocks of 32 with s2_tile up to 512; at
+// most kPrefixMax (batch, head group, row block) units.
 bool rows_path_supported(int nkv, int s2_tile, int rows, int s1, int nq, int B) {
     (void)s1;
     (void)nq;
-    const bool tile_ok = s2_tile == 128 || s2_tile == 256 || s2_tile == 512 || (s2_tile == 1024 && rows <= 16);
-    return tile_ok && rows >= 1 && rows <= 32 && (int64_t)B * (nkv / rows_group(nkv)) <= kPrefixMax;
+    const int rbk = rows_row_blocks(rows);
+    const bool tile_ok = s2_tile == 128 || s2_tile == 256 || s2_tile == 512 ||
+                         (s2_tile == 1024 && rows <= 16);
+    return tile_ok && rows >= 1 && (int64_t)B * rbk * (nkv / rows_group(nkv)) <= kPrefixMax;
 }
 
 hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t st, bool dbg) {

@@ -113,17 +113,19 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
  * Two kernels serve the call (same results within the stated tolerance):
  *  - num_splits == 0 and the shape inside the whole-row path's limits: one
  *    workgroup per CU streams a cost-balanced range of (batch, KV-head pair,
- *    tile) units and a small second kernel merges split sequences.  Limits:
- *    s1 * nq / nkv <= 32 query rows per KV head (<= 16 with s2_tile 1024;
- *    s2_tile 2048 is not served) and B * ceil(nkv / 2) <= 1024 (batch, head
- *    pair) units (nkv odd: B * nkv <= 1024).
+ *    block of query rows, tile) units and a small second kernel merges split
+ *    sequences.  A KV head's s1 * nq / nkv query rows form one block when
+ *    there are at most 32 of them, else blocks of 32, each streaming the
+ *    sequence's K and V.  Limits: s2_tile 128, 256 or 512 (1024 only with at
+ *    most 16 query rows per KV head; 2048 is not served) and
+ *    B * (row blocks) * ceil(nkv / 2) <= 1024 units (nkv odd: nkv in place of
+ *    ceil(nkv / 2)).
  *  - otherwise (an explicit num_splits, or a shape outside those limits,
- *    e.g. B >= 257 at nkv = 8, or more than 32 query rows per KV head): one
- *    workgroup per (batch, KV head, block of query rows, split) -- all of a
- *    KV head's rows when they are at most 64, else blocks of 32 -- with the
- *    split count chosen from the table capacity.  It is the slower path for
- *    large batches of short sequences; choose shapes inside the whole-row
- *    limits where speed matters.
+ *    e.g. B >= 257 at nkv = 8): one workgroup per (batch, KV head, block of
+ *    query rows, split) -- all of a KV head's rows when they are at most 64,
+ *    else blocks of 32 -- with the split count chosen from the table capacity
+ *    (no split once there are 1024 or more such units).  It is the slower
+ *    path; choose shapes inside the whole-row limits where speed matters.
  */
 pa_status_t pa_fp8_decode(const void* q_dev, const float* q_scale_dev,
                           const uint8_t* k_cache_dev, const float* k_scale_dev,
@@ -189,9 +191,10 @@ pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev,
  * be a prefill chunk (hundreds of positions).  Each position keeps its own
  * tiles over [0, n_s) (P quantised per row over the tile's tokens that row
  * sees); n_s = 0 gives a zero row.  Same arguments, workspace, split count
- * and paths as pa_fp8_decode: the whole-row path when num_splits == 0 and the
- * shape is inside its limits, else the per-head path, which takes any number
- * of query rows per KV head (blocks of 32 rows when there are more than 64).
+ * and paths as pa_fp8_decode: the whole-row path (query rows in blocks of 32
+ * when there are more than 32) when num_splits == 0 and the shape is inside its
+ * limits, else the per-head path, which takes any number of query rows per KV
+ * head (blocks of 32 rows when there are more than 64).
  */
 pa_status_t pa_fp8_decode_causal(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
                                  const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,

@@ -294,6 +294,26 @@ def test_long_s1_non_causal_parity(B, oracle_mod):
         compare(_run(B, inp, ns, "long s1"), ref, f"long s1 non-causal splits={ns}")
 
 
+def test_row_blocks_dumps_bit_exact(B, oracle_mod):
+    """The whole-row path with a KV head's rows in blocks of 32 (s1 = 6, G = 11:
+    66 rows, the last block of 2): the gathered rows and the query codes dumped
+    from inside the kernel equal the oracle's, and so does the output."""
+    cfg = _case("row-blocks", B=5, s1=6, nq=22, nkv=2, s2_tile=512, seq_lens=(1300, 1, 640, 0, 2049),
+                num_blocks=60, max_blocks_per_seq=17, seed=83)
+    inp = synth.make_gqa_inputs(cfg)
+    ref = oracle_mod.gqa_decode(inp)
+    d = to_device(inp)
+    print("[gpu] row-block dumps", flush=True)
+    out, rows, q8 = B.decode_debug(d["q"], d["q_scale"], d["k_cache"], d["k_scale"], d["v_cache"], d["v_scale"],
+                                   d["block_table"], d["kv_act_seqs"], d["softmax_scale"], cfg.s2_tile, s1=cfg.s1)
+    torch.cuda.synchronize()
+    assert np.array_equal(rows.cpu().numpy(), ref["rows"])
+    assert np.array_equal(q8.cpu().numpy(), ref["q8"])
+    compare(gpu_out_float(out), ref, "row-block debug")
+    for ns in (0, 3):
+        compare(_run(B, inp, ns, "row blocks"), ref, f"row blocks splits={ns}")
+
+
 @pytest.mark.parametrize("num_splits", [0, 2])
 def test_prefill_causal_poison_bit_identical(B, num_splits):
     """NaN codes and scales past every sequence change no output bit of the
