@@ -26,6 +26,8 @@
 //    workgroup writes an (O, M, L) partial and a second, small kernel merges
 //    them (the kernel boundary orders the writes; no fences or atomics).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "pa_fp8_common.h"
@@ -151,7 +153,9 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
     __shared__ __attribute__((aligned(16))) uint8_t s_q[2][QROWS * 256];
     __shared__ __attribute__((aligned(16))) float s_qs[2][64];
     __shared__ __attribute__((aligned(16))) float s_vs[2][256];
-    __shared__ __attribute__((aligned(16))) float s_comb[HG][16 * kHeadDim + 16];
+    // sequence ends: each token-half wave's outgoing four columns of O (4 rows x 64 lanes x
+    // f32x4 per wave) and its 16 row sums, per head
+    __shared__ __attribute__((aligned(16))) float s_comb[HG][2 * 1024 + 2 * 16];
     __shared__ __attribute__((aligned(16))) float s_max[NW][R];
     __shared__ __attribute__((aligned(16))) float s_qpad[NW][64];
     __shared__ int s_pref[kPrefixMax + 1];   // exclusive cost prefix over (batch, group), in steps
@@ -750,38 +754,38 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
             }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                // the two halves of each head: wave p = 1 hands its O and L to wave p = 0
-                float Lw = wave_sum_over_groups(L_s[rb]);
-                if (p == 1) {
+                // the two token halves of each head: wave p finishes output columns
+                // 8 lr + [4p, 4p + 4) of every row and hands the other four columns of its O,
+                // and its L, to its partner (wave p ^ 1) through LDS
+                const float Lw = wave_sum_over_groups(L_s[rb]);
+                auto handoff = [&](auto P) {
+                    constexpr int PH = decltype(P)::value, OT = 4 * (1 - PH);
+                    float* dst = &s_comb[hl][PH * 1024];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float* dst = &s_comb[hl][(4 * lg + i) * kHeadDim + 8 * lr];
-                        *reinterpret_cast<f32x4*>(dst) = f32x4{O[rb][0][i], O[rb][1][i], O[rb][2][i], O[rb][3][i]};
-                        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{O[rb][4][i], O[rb][5][i], O[rb][6][i], O[rb][7][i]};
-                    }
-                    if (lg == 0) s_comb[hl][16 * kHeadDim + lr] = Lw;
-                }
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<f32x4*>(dst + (i * 64 + lane) * 4) =
+                            f32x4{O[rb][OT][i], O[rb][OT + 1][i], O[rb][OT + 2][i], O[rb][OT + 3][i]};
+                    if (lg == 0) s_comb[hl][2048 + 16 * PH + lr] = Lw;
+                };
+                if (p == 0) handoff(std::integral_constant<int, 0>{});
+                else handoff(std::integral_constant<int, 1>{});
                 wait_lgkm();
                 barrier_nofence();
-                if (p == 0) {
+                auto finish = [&](auto P) {
+                    constexpr int PH = decltype(P)::value, MY = 4 * PH;
+                    const float* src = &s_comb[hl][(1 - PH) * 1024];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float* src = &s_comb[hl][(4 * lg + i) * kHeadDim + 8 * lr];
-                        const f32x4 o0 = *reinterpret_cast<const f32x4*>(src);
-                        const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + 4);
+                        const f32x4 o = *reinterpret_cast<const f32x4*>(src + (i * 64 + lane) * 4);
 #pragma unroll
-                        for (int cc = 0; cc < 4; ++cc) {
-                            O[rb][cc][i] += o0[cc];
-                            O[rb][4 + cc][i] += o1[cc];
-                        }
+                        for (int cc = 0; cc < 4; ++cc) O[rb][MY + cc][i] += o[cc];
                     }
-                    Lw += s_comb[hl][16 * kHeadDim + lr];
-                    const f32x4 vs0 = *reinterpret_cast<const f32x4*>(&s_vs[vs_buf][hl * kHeadDim + 8 * lr]);
-                    const f32x4 vs1 = *reinterpret_cast<const f32x4*>(&s_vs[vs_buf][hl * kHeadDim + 8 * lr + 4]);
+                    const float Lt = Lw + s_comb[hl][2048 + 16 * (1 - PH) + lr];
+                    const f32x4 vs = *reinterpret_cast<const f32x4*>(&s_vs[vs_buf][hl * kHeadDim + 8 * lr + MY]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int rr = rb * 16 + 4 * lg + i;
-                        const float Lr = __shfl(Lw, 4 * lg + i, 64);
+                        const float Lr = __shfl(Lt, 4 * lg + i, 64);
                         if (rr >= cur_rows) continue;
                         const int ra = 32 * cur.rk + rr;
                         const int s = small_div(ra, inv_g), gq = ra - s * a.G;
@@ -789,29 +793,24 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                         if (!split) {
                             // step 10: out = O * v_scale / L' (L' = 448 L), bf16
                             const float inv = Lr > 0.f ? 1.f / Lr : 0.f;     // no token at all (causal): zeros
-                            uint32_t pk[4];
-#pragma unroll
-                            for (int q2 = 0; q2 < 4; ++q2) {
-                                const int c0 = 2 * q2, c1 = 2 * q2 + 1;
-                                const float x0 = O[rb][c0][i] * (c0 < 4 ? vs0[c0] : vs1[c0 - 4]) * inv;
-                                const float x1 = O[rb][c1][i] * (c1 < 4 ? vs0[c1] : vs1[c1 - 4]) * inv;
-                                pk[q2] = pack_bf16x2(x0, x1);
-                            }
-                            *reinterpret_cast<i32x4*>(a.out + qrow * kHeadDim + 8 * lr) =
-                                i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+                            const uint32_t pk0 = pack_bf16x2(O[rb][MY][i] * vs[0] * inv, O[rb][MY + 1][i] * vs[1] * inv);
+                            const uint32_t pk1 =
+                                pack_bf16x2(O[rb][MY + 2][i] * vs[2] * inv, O[rb][MY + 3][i] * vs[3] * inv);
+                            *reinterpret_cast<uint2*>(a.out + qrow * kHeadDim + 8 * lr + MY) = uint2{pk0, pk1};
                         } else {
-                            const int64_t slot = slot_base;
-                            float* po = a.part_o + (slot * R + rr) * kHeadDim + 8 * lr;
-                            *reinterpret_cast<f32x4*>(po) = f32x4{O[rb][0][i], O[rb][1][i], O[rb][2][i], O[rb][3][i]};
-                            *reinterpret_cast<f32x4*>(po + 4) = f32x4{O[rb][4][i], O[rb][5][i], O[rb][6][i], O[rb][7][i]};
-                            if (lr == 0) {
-                                float* pm = a.part_ml + (slot * R + rr) * 2;
+                            float* po = a.part_o + (slot_base * R + rr) * kHeadDim + 8 * lr + MY;
+                            *reinterpret_cast<f32x4*>(po) =
+                                f32x4{O[rb][MY][i], O[rb][MY + 1][i], O[rb][MY + 2][i], O[rb][MY + 3][i]};
+                            if (PH == 0 && lr == 0) {
+                                float* pm = a.part_ml + (slot_base * R + rr) * 2;
                                 pm[0] = M_o[rb][i];
                                 pm[1] = Lr;
                             }
                         }
                     }
-                }
+                };
+                if (p == 0) finish(std::integral_constant<int, 0>{});
+                else finish(std::integral_constant<int, 1>{});
                 if (NRB > 1) {                        // s_comb is reused by the next row block
                     wait_lgkm();
                     barrier_nofence();
