@@ -529,43 +529,59 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_rows_kernel(DecodeParams a
                 if (r == 0 && seg_start) {
                     const unsigned long long ph_a = PH_NOW();
                     ++ph_segs;
-                    // step 1: this head's query rows -> bf16 operands of exact FP8 codes
+                    // step 1: this head's query rows -> bf16 operands of exact FP8 codes.  The two
+                    // token-half waves of a head need the same operands: wave p converts the
+                    // values of half p of each row (MFMA operands 2p, 2p + 1) and the halves are
+                    // swapped through LDS (free here: the last sequence end is behind a barrier).
+                    auto convert = [&](auto P) {
+                        constexpr int PH = decltype(P)::value;
 #pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) {
-                        const int rr = rb * 16 + lr;
-                        uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                        qcoef[rb] = 0.f;
-                        // causal decode: position s of s1 attends to the first seq - s1 + 1 + s tokens
-                        const int ra = 32 * cur.rk + rr;           // the row among the head's s1 G
-                        lim[rb] = cur.seq - (a.causal ? a.s1 - 1 - (rr < cur_rows ? small_div(ra, inv_g) : a.s1 - 1) : 0);
-                        mlim = cur.seq - (a.causal ? a.s1 - 1 : 0);
-                        if (rr < cur_rows) {
-                            const int sr = hl * qstride + rr;
-                            const float qs = s_qs[vs_buf][sr];
-                            qcoef[rb] = qs * a.softmax_scale * kLog2e;
-                            const QRecip qd = q_recip(qs);
-#pragma unroll
-                            for (int hlf = 0; hlf < 2; ++hlf) {
-                                const uint8_t* qp = s_q[vs_buf] + sr * 256 + (hlf * 64 + 16 * lg) * 2;
+                        for (int rb = 0; rb < NRB; ++rb) {
+                            const int rr = rb * 16 + lr;
+                            uint32_t wds[4] = {0, 0, 0, 0};
+                            qcoef[rb] = 0.f;
+                            // causal decode: position s of s1 attends to the first seq - s1 + 1 + s tokens
+                            const int ra = 32 * cur.rk + rr;       // the row among the head's s1 G
+                            lim[rb] = cur.seq - (a.causal ? a.s1 - 1 - (rr < cur_rows ? small_div(ra, inv_g) : a.s1 - 1) : 0);
+                            mlim = cur.seq - (a.causal ? a.s1 - 1 : 0);
+                            if (rr < cur_rows) {
+                                const int sr = hl * qstride + rr;
+                                const float qs = s_qs[vs_buf][sr];
+                                qcoef[rb] = qs * a.softmax_scale * kLog2e;
+                                const uint8_t* qp = s_q[vs_buf] + sr * 256 + (PH * 64 + 16 * lg) * 2;
                                 const i32x4 v0 = *reinterpret_cast<const i32x4*>(qp);
                                 const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + 16);
                                 const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
                                                          (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
-                                quantise_q16(raw, qd, &wds[hlf * 4]);
+                                quantise_q16(raw, q_recip(qs), wds);
+                                if (DBG && a.dbg_q8) {
+                                    const int s = small_div(ra, inv_g), gq = ra - s * a.G;
+                                    const int64_t qrow = ((int64_t)cur.br * a.s1 + s) * a.nq + h * a.G + gq;
+                                    uint8_t* dst = a.dbg_q8 + qrow * kHeadDim + PH * 64 + 16 * lg;
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(dst + 4 * i) = wds[i];
+                                }
                             }
-                            if (DBG && a.dbg_q8 && p == 0) {
-                                const int s = small_div(ra, inv_g), gq = ra - s * a.G;
-                                const int64_t qrow = ((int64_t)cur.br * a.s1 + s) * a.nq + h * a.G + gq;
-                                uint8_t* dst = a.dbg_q8 + qrow * kHeadDim;
 #pragma unroll
-                                for (int hlf = 0; hlf < 2; ++hlf)
-#pragma unroll
-                                    for (int i = 0; i < 4; ++i)
-                                        *reinterpret_cast<uint32_t*>(dst + hlf * 64 + 16 * lg + 4 * i) = wds[hlf * 4 + i];
+                            for (int ii = 0; ii < 2; ++ii) {
+                                qop[rb][2 * PH + ii] = fp8x8_to_op(wds[2 * ii], wds[2 * ii + 1]);
+                                *reinterpret_cast<bf16x8*>(&s_comb[hl][PH * NRB * 512 + ((rb * 2 + ii) * 64 + lane) * 4]) =
+                                    qop[rb][2 * PH + ii];
                             }
                         }
+                        wait_lgkm();
+                        barrier_nofence();
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) qop[rb][i] = fp8x8_to_op(wds[2 * i], wds[2 * i + 1]);
+                        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                            for (int ii = 0; ii < 2; ++ii)
+                                qop[rb][2 * (1 - PH) + ii] = *reinterpret_cast<const bf16x8*>(
+                                    &s_comb[hl][(1 - PH) * NRB * 512 + ((rb * 2 + ii) * 64 + lane) * 4]);
+                    };
+                    if (p == 0) convert(std::integral_constant<int, 0>{});
+                    else convert(std::integral_constant<int, 1>{});
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) {
                         M_s[rb] = -INFINITY;
                         L_s[rb] = 0.f;
 #pragma unroll
