@@ -76,6 +76,40 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w0, uint32_t w1, const float
     return r;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at dst + 16 i.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_to_lds(const void* src, lds_ptr dst) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "s"(m) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) (gfx9 encoding, lgkmcnt and expcnt left at their maxima): this
+// wave's vector memory operations complete in issue order.  The scheduling barriers
+// keep the compiler from moving the work of the previous block below the wait.
+template <int N>
+__device__ __forceinline__ void mla_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// gfx950 transposing LDS read of 8-bit data.  In each group of 16 lanes, lanes
+// 2j + h (j = 0..7, h = 0..1) name 8-byte chunks; lane 8h + c receives byte c of
+// each of the 8 chunks named by lanes 2j + h, byte j from lane 2j + h.
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+
+// Workgroup barrier that is also a compiler memory barrier, without the release
+// fence of __syncthreads (which would wait for every load in flight).
+__device__ __forceinline__ void barrier_nofence_mla() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int T, int NWV>
 __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     constexpr int RW = T / NWV;           // rows of the tile whose scores a wave computes
@@ -92,6 +126,14 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_p[NB][2][64 * 16];   // BF16 P, MFMA A-operand layout
     __shared__ float s_max[NWV][kMlaHeads], s_sum[NWV][kMlaHeads];
     __shared__ __attribute__((aligned(16))) uint8_t s_qop[2][18][64 * 16];  // Q as MFMA B operands, per lane
+    // ring of 32-row V blocks (nope codes, 512 bytes a row), filled by DMA; 16-byte piece p of
+    // row r sits in slot p ^ (r & 15) so that the transposing reads of one 16-channel column
+    // spread over the banks
+    constexpr int NBUF = 3;
+    static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+    constexpr int DPW = 16 / NWV;         // DMA instructions (two rows each) per wave per block
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[NBUF][32 * 512];
+    __shared__ __attribute__((aligned(16))) float s_sc[4][T];   // group scales by row, 0 past n
 
     PH_STAMP(0);
     const int lane = threadIdx.x & 63;
@@ -136,6 +178,9 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
         s_noff[i] = r * a.nope_stride;
         s_roff[i] = r * a.rope_stride;
         s_soff[i] = r * a.scale_stride;
+        const f32x4 g = *reinterpret_cast<const f32x4*>(a.scales + r * a.scale_stride);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s_sc[k][i] = row < 0 ? 0.f : g[k];
     }
 
     // ---- query operands: heads h0 + 16 hh + lr; k-slot order shared with K ----------------
@@ -152,6 +197,22 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
     __syncthreads();
     PH_STAMP(1);
     auto qop = [&](int hh, int ks) { return *reinterpret_cast<const bf16x8*>(&s_qop[hh][ks][16 * lane]); };
+
+    // V block bi (rows 32 bi .. 32 bi + 31 of the tile) into ring slot bi % NBUF: this wave's
+    // DMA instructions cover rows 2 i and 2 i + 1 for i in [DPW w, DPW w + DPW)
+    auto issue_vblock = [&](int bi) {
+#pragma unroll
+        for (int d = 0; d < DPW; ++d) {
+            const int i = DPW * w + d;
+            const int r = 2 * i + (lane >> 5);
+            const int piece = (lane & 31) ^ (r & 15);
+            dma16_to_lds(a.nope + s_noff[32 * bi + r] + 16 * piece, (lds_ptr)&s_v[bi % NBUF][1024 * i]);
+        }
+    };
+    constexpr int NBV = T / 32;
+#pragma unroll
+    for (int bi = 0; bi < NBUF - 1; ++bi)
+        if (bi < NBV) issue_vblock(bi);
 
     // ---- scores of this wave's rows: S^T (rows x heads), log2 units ------------------------
     const float coef = a.softmax_scale * kLog2e;
@@ -244,67 +305,54 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
 
     PH_STAMP(4);
     // ---- P.V for channels [CPW w, CPW w + CPW): O[head][channel] -------------------------
+    // MFMA c takes channels CPW w + 16 c + [0, 16); lane (n, g) holds channel n of rows
+    // chunk_token(g, j), j = 0..7, the rows of the P operand's k-slots.
     f32x4 O[2][CL];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int c = 0; c < CL; ++c) O[hh][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int grp = CPW * w / 128;                            // the channels' scale group
-    // the V rows of block bi + PD are requested while block bi is multiplied
-    constexpr int PD = CL == 8 ? 5 : 6;
-    uint32_t xq[PD][8][CL / 4];
-    float sq[PD][8];
-    int negq[PD];
-    auto issue_v = [&](int bi, uint32_t (&x)[8][CL / 4], float (&sc)[8], int& neg) {
-        neg = 0;
+    // transposing reads: lane 2 j + h of each 16-lane group names row chunk_token(g, j),
+    // bytes 8 h .. 8 h + 7 of the 16-channel column
+    const int tr_r = chunk_token(lg, (lane & 15) >> 1);
+    int tr_off[CL];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int idx = 32 * bi + chunk_token(lg, j);
-            const int row = s_row[idx];
-            const uint8_t* vp = a.nope + s_noff[idx] + CPW * w + CL * lr;
-            if (CL == 8) {
-                const uint2 v2 = *reinterpret_cast<const uint2*>(vp);
-                x[j][0] = v2.x;
-                x[j][CL / 4 - 1] = v2.y;
-            } else {
-                x[j][0] = *reinterpret_cast<const uint32_t*>(vp);
-            }
-            // a position past n reads row 0, whose scale may be NaN / Inf: use 0 so that
-            // its zeroed codes dequantise to 0 and P = 0 multiplies a finite value
-            const float scv = *reinterpret_cast<const float*>(a.scales + s_soff[idx] + 4 * grp);
-            sc[j] = row < 0 ? 0.f : scv;
-            neg |= (row < 0) << j;
-        }
-    };
-#pragma unroll
-    for (int i = 0; i < PD; ++i)
-        if (i < NB) issue_v(i, xq[i], sq[i], negq[i]);
+    for (int c = 0; c < CL; ++c) tr_off[c] = tr_r * 512 + 16 * ((CPW * w / 16 + c) ^ (tr_r & 15)) + 8 * (lane & 1);
+    const int nvalid = n - t * T;                             // valid rows of this tile (> 0)
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
-        const int q = bi % PD;
+        // this wave's DMA of block bi has landed once only the younger blocks' remain
+        {
+            const int younger = (NB - 1 - bi < NBUF - 2) ? NB - 1 - bi : NBUF - 2;
+            if (younger >= 2) mla_wait_vm<2 * DPW>();
+            else if (younger == 1) mla_wait_vm<DPW>();
+            else mla_wait_vm<0>();
+        }
+        if (32 * bi + 32 > nvalid) {
+            // rows past n read row 0, whose codes may be NaN: zero the rows this wave loaded
+#pragma unroll
+            for (int d = 0; d < DPW; ++d)
+#pragma unroll
+                for (int hr = 0; hr < 2; ++hr) {
+                    const int r = 2 * (DPW * w + d) + hr;
+                    if (32 * bi + r >= nvalid)
+                        *reinterpret_cast<uint2*>(&s_v[bi % NBUF][r * 512 + 8 * lane]) = uint2{0u, 0u};
+                }
+        }
+        barrier_nofence_mla();
+        if (bi + NBUF - 1 < NB) issue_vblock(bi + NBUF - 1);   // into the slot block bi - 1 used
         bf16x8 pop[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) pop[hh] = *reinterpret_cast<const bf16x8*>(&s_p[bi][hh][16 * lane]);
-        uint32_t xl[8], xh[8];
-        float scj[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool neg = (negq[q] >> j) & 1;            // positions past n: zero codes (P is 0 there)
-            xl[j] = neg ? 0u : xq[q][j][0];
-            xh[j] = neg ? 0u : xq[q][j][CL / 4 - 1];
-            scj[j] = sq[q][j];
-        }
-        if (bi + PD < NB) issue_v(bi + PD, xq[q], sq[q], negq[q]);
-        uint32_t ylo[8], yhi[8];
-        transpose4(xl[0], xl[1], xl[2], xl[3], ylo[0], ylo[1], ylo[2], ylo[3]);
-        transpose4(xl[4], xl[5], xl[6], xl[7], yhi[0], yhi[1], yhi[2], yhi[3]);
-        if (CL == 8) {
-            transpose4(xh[0], xh[1], xh[2], xh[3], ylo[4], ylo[5], ylo[6], ylo[7]);
-            transpose4(xh[4], xh[5], xh[6], xh[7], yhi[4], yhi[5], yhi[6], yhi[7]);
-        }
+        const f32x4 sa = *reinterpret_cast<const f32x4*>(&s_sc[grp][32 * bi + 4 * lg]);
+        const f32x4 sb = *reinterpret_cast<const f32x4*>(&s_sc[grp][32 * bi + 16 + 4 * lg]);
+        const float scj[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+        const uint8_t* vb = &s_v[bi % NBUF][0];
 #pragma unroll
         for (int c = 0; c < CL; ++c) {
-            const bf16x8 vop = dequant8(ylo[c], yhi[c], scj);      // channel CPW w + CL lr + c, 8 rows
+            const i32x2 x = lds_read_tr8(vb + tr_off[c]);
+            const bf16x8 vop = dequant8((uint32_t)x[0], (uint32_t)x[1], scj);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) O[hh][c] = mfma_bf16(pop[hh], vop, O[hh][c]);
         }
@@ -318,11 +366,9 @@ __global__ __launch_bounds__(NWV * 64) void mla_decode_kernel(MlaParams a) {
         for (int i = 0; i < 4; ++i) {
             const int head = h0 + 16 * hh + 4 * lg + i;
             const int64_t slot = ((int64_t)bs * a.nq + head) * a.ntiles_max + t;
-            float* po = a.part_o + slot * kMlaNope + CPW * w + CL * lr;
+            float* po = a.part_o + slot * kMlaNope + CPW * w + lr;
 #pragma unroll
-            for (int c4 = 0; c4 < CL / 4; ++c4)
-                *reinterpret_cast<f32x4*>(po + 4 * c4) =
-                    f32x4{O[hh][4 * c4][i], O[hh][4 * c4 + 1][i], O[hh][4 * c4 + 2][i], O[hh][4 * c4 + 3][i]};
+            for (int c = 0; c < CL; ++c) po[16 * c] = O[hh][c][i];
         }
         if (w == 0 && lg == 0) {
             const int hc = 16 * hh + lr;
