@@ -41,11 +41,13 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
-    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma", "phases"], default="decode",
+    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma", "phases", "valu-rates"],
+                    default="decode",
                     help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
                          "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows; "
                          "ceiling: read-only probes of config 1's paged access pattern and of a contiguous "
-                         "buffer, beside the decode")
+                         "buffer, beside the decode; valu-rates: issue rate of the FP8 dequantisation "
+                         "instructions")
     ap.add_argument("--no-secondary", action="store_true",
                     help="headline only: skip the other workloads' entries")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -186,6 +188,8 @@ def main():
         return run_fp8_mfma(args)
     if args.op == "phases":
         return run_phases(args)
+    if args.op == "valu-rates":
+        return run_valu_rates(args)
     if args.config == 4:
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
@@ -486,6 +490,46 @@ def run_ceiling(args):
                    "kernel": "pa::decode_rows_kernel + pa::merge_rows_kernel"},
     }
     print(json.dumps(line), flush=True)
+
+
+def run_valu_rates(args):
+    """Issue rate of the VALU instructions that turn FP8 codes into MFMA operands, from
+    the probe library: every SIMD of the chip busy with 8 waves (2048 workgroups of
+    256 threads), each wave running 8 independent chains; event-timed."""
+    import ctypes
+    import torch
+    from fp8_paged_kv_amd import build
+    P = ctypes.CDLL(build.PROBE_LIB)
+    P.pa_probe_valu_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    P.pa_probe_valu_rate.restype = ctypes.c_int
+    names = ["v_mul_f32", "v_cvt_pk_f32_fp8 (2 codes -> 2 FP32)", "v_cvt_pk_bf16_f32 (2 FP32 -> 2 BF16, RNE)",
+             "v_cvt_scalef32_pk_bf16_fp8 (2 codes -> 2 BF16)", "v_perm_b32", "v_fma_f32"]
+    grid, threads, iters = 2048, 256, 4096
+    simds = torch.cuda.get_device_properties(0).multi_processor_count * 4
+    sink = torch.empty(grid * threads, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for op, name in enumerate(names):
+        for _ in range(2):
+            if P.pa_probe_valu_rate(op, grid, threads, iters, sink.data_ptr(), st) != 0:
+                sys.exit(f"probe launch failed for {name}")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            P.pa_probe_valu_rate(op, grid, threads, iters, sink.data_ptr(), st)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        per_simd = grid * (threads // 64) * iters * 8 / simds       # wave instructions per SIMD
+        res[name] = {"ns_per_wave_instruction_per_simd": round(t / per_simd * 1e9, 4),
+                     "cycles_at_2.4GHz": round(t / per_simd * 2.4e9, 2)}
+    base = res[names[0]]["ns_per_wave_instruction_per_simd"]
+    for name in names:
+        res[name]["relative_to_v_mul_f32"] = round(res[name]["ns_per_wave_instruction_per_simd"] / base, 2)
+    print(json.dumps({"metric": "VALU issue rate, wave64 instructions", "simds": simds,
+                      "waves_per_simd": grid * (threads // 64) / simds, "rates": res}), flush=True)
 
 
 def run_fp8_mfma(args):

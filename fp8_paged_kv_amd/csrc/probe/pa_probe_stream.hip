@@ -12,6 +12,8 @@
 //    dispatcher balancing the load;
 //  * probe_contiguous_kernel: a plain contiguous read of a buffer with 16-byte
 //    loads, grid-strided.
+// Beside them: the FP8 MFMA against exact sums, and the issue rate of the VALU
+// instructions that dequantise FP8 codes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -164,9 +166,71 @@ __global__ __launch_bounds__(64) void probe_fp8_mfma_kernel(const uint8_t* a, co
     }
 }
 
+// Issue rate of one VALU instruction: every wave runs `iters` rounds of eight
+// independent instances (eight dependency chains), so with several waves per SIMD
+// the SIMD's issue rate, not latency, sets the time.  OP: 0 v_mul_f32,
+// 1 v_cvt_pk_f32_fp8, 2 v_cvt_pk_bf16_f32, 3 v_cvt_scalef32_pk_bf16_fp8,
+// 4 v_perm_b32, 5 v_fma_f32.  sink: one word per thread.
+template <int OP>
+__global__ void probe_valu_rate_kernel(int iters, float* sink) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    float f[8];
+    uint32_t u[8];
+    for (int i = 0; i < 8; ++i) {
+        f[i] = 1.0f + 0.001f * (float)(threadIdx.x + i);
+        u[i] = 0x38403840u + 0x01010101u * (uint32_t)i + threadIdx.x;
+    }
+    const float sc = 1.0009765625f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (OP == 0) {
+                asm volatile("v_mul_f32 %0, %0, %1" : "+v"(f[i]) : "v"(sc));
+            } else if (OP == 1) {
+                f32x2 r;
+                asm volatile("v_cvt_pk_f32_fp8 %0, %1" : "=v"(r) : "v"(u[i]));
+                u[i] ^= __builtin_bit_cast(uint32_t, r.x) >> 16;
+            } else if (OP == 2) {
+                uint32_t r;
+                asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(f[i]), "v"(sc));
+                f[i] = __builtin_bit_cast(float, (r & 0x007fffffu) | 0x3f800000u);
+            } else if (OP == 3) {
+                uint32_t r;
+                asm volatile("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2" : "=v"(r) : "v"(u[i]), "v"(sc));
+                u[i] ^= r >> 16;
+            } else if (OP == 4) {
+                asm volatile("v_perm_b32 %0, %0, %1, %2" : "+v"(u[i]) : "v"(u[(i + 1) & 7]), "v"(0x05010400u));
+            } else {
+                asm volatile("v_fma_f32 %0, %0, %1, %1" : "+v"(f[i]) : "v"(sc));
+            }
+        }
+    }
+    float acc = 0.f;
+    for (int i = 0; i < 8; ++i) acc += f[i] + (float)(u[i] & 0xffu);
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// VALU issue-rate probe: `grid` workgroups of `threads` threads (a multiple of 64, at
+// most 1024), each wave running iters x 8 instructions of kind `op` (see
+// probe_valu_rate_kernel).  sink: grid * threads floats.  Returns 0 or a hipError_t.
+int pa_probe_valu_rate(int op, int grid, int threads, int iters, float* sink, void* stream) {
+    if (grid <= 0 || threads <= 0 || threads > 1024 || threads % 64 || iters <= 0 || op < 0 || op > 5)
+        return (int)hipErrorInvalidValue;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (op) {
+        case 0: hipLaunchKernelGGL(probe_valu_rate_kernel<0>, dim3(grid), dim3(threads), 0, st, iters, sink); break;
+        case 1: hipLaunchKernelGGL(probe_valu_rate_kernel<1>, dim3(grid), dim3(threads), 0, st, iters, sink); break;
+        case 2: hipLaunchKernelGGL(probe_valu_rate_kernel<2>, dim3(grid), dim3(threads), 0, st, iters, sink); break;
+        case 3: hipLaunchKernelGGL(probe_valu_rate_kernel<3>, dim3(grid), dim3(threads), 0, st, iters, sink); break;
+        case 4: hipLaunchKernelGGL(probe_valu_rate_kernel<4>, dim3(grid), dim3(threads), 0, st, iters, sink); break;
+        default: hipLaunchKernelGGL(probe_valu_rate_kernel<5>, dim3(grid), dim3(threads), 0, st, iters, sink); break;
+    }
+    return (int)hipGetLastError();
+}
 
 // FP8 MFMA probe: `count` independent 16x16x32 products (a, b: count * 512 code
 // bytes; c, c_ref: count * 256 floats).  Returns 0 or a hipError_t.
