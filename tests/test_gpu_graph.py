@@ -73,11 +73,13 @@ def test_gqa_decode_graph_replays(B, num_splits):
     _check_replays(run_eager, run_into, outs, f"gqa splits={num_splits}")
 
 
-def test_mla_decode_graph_replays(B):
-    cfg = synth.MlaConfig("graph-mla", B=2, s1=1, nq=32, topk=512, seq_range=(600, 1500), num_blocks=32,
-                          max_blocks_per_seq=16, s2_tile=256, seed=33)
+@pytest.mark.parametrize("nq,s2_tile", [(32, 256), (64, 512)])
+def test_mla_decode_graph_replays(B, nq, s2_tile):
+    """Captured MLA calls replay the eager result (32- and 64-head query groups)."""
+    cfg = synth.MlaConfig("graph-mla", B=2, s1=2, nq=nq, topk=1024, seq_range=(600, 1500), num_blocks=32,
+                          max_blocks_per_seq=16, s2_tile=s2_tile, seed=33)
     inp = synth.make_mla_inputs(cfg, device="cuda")
-    print("[gpu] graph replays, mla decode", flush=True)
+    print(f"[gpu] graph replays, mla decode nq={nq} s2_tile={s2_tile}", flush=True)
     ws = torch.zeros(max(B.mla_workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.topk, cfg.s2_tile), 1),
                      dtype=torch.uint8, device="cuda")
     shape = (cfg.B * cfg.s1 * cfg.nq, 512)

@@ -208,3 +208,30 @@ def test_mla_several_kv_heads(B, oracle_mod, nkv):
     g1 = got.reshape(-1, nq, 512)
     assert np.array_equal(got2[:, :32], g1[:, 32:64]) and np.array_equal(got2[:, 32:64], g1[:, :32])
     assert np.array_equal(got2[:, 64:], g1[:, 64:])
+
+
+@pytest.mark.parametrize("nq,nkv", [(64, 1), (128, 2), (192, 1)])
+def test_mla_wide_query_groups_parity(B, oracle_mod, nq, nkv):
+    """Query groups of 64, 64 and 192 heads (several 32-head workgroups per tile) at
+    s2_tile 512, s1 = 2 and lengths 0, 100, 300, 700 and 1500 under topk 1024: empty
+    rows, a tile whose second half holds no valid row, tiles ending part-way and two
+    tiles."""
+    inp = synth.make_mla_inputs(_cfg(f"mla-groups-{nq}-{nkv}", nq=nq, nkv=nkv, s1=2, topk=1024, B=5,
+                                     seq_lens=(0, 100, 300, 700, 1500), num_blocks=80, seed=41 + nq))
+    compare(gpu_out_float(_run(B, inp, f"groups nq={nq} nkv={nkv}")), oracle_mod.mla_decode(inp),
+            f"mla groups nq={nq} nkv={nkv}")
+
+
+def test_mla_wide_group_poison_and_kv_split(B, oracle_mod):
+    """A 64-head query group under the poisoned cache (NaN / Inf in every unselected
+    row, row 0 among them) gives the clean output bit for bit, in both layouts."""
+    inp = synth.make_mla_inputs(_cfg("mla-groups-poison", nq=64, s1=2, topk=1024, seq_lens=(300, 1500, 700), B=3,
+                                     num_blocks=60, s2_tile=512, seed=17))
+    dirty, bad = _poison_mla(inp)
+    assert bool(bad[0]), "row 0 must be one of the poisoned rows"
+    clean = _run(B, inp, "groups poison clean")
+    got = _run(B, dirty, "groups poison dirty")
+    assert torch.equal(clean, got)
+    compare(gpu_out_float(got), oracle_mod.mla_decode(inp), "mla groups poison")
+    split = _run_split(B, dirty, "groups poison")
+    assert torch.equal(clean, split)
