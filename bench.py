@@ -319,6 +319,14 @@ def causal_flops(cfg, seqs):
     return 4 * cfg.D * G * cfg.nkv * tok
 
 
+def prefill_path(cfg):
+    """Whether the library runs this shape on its prefill kernel (the header's rule for
+    num_splits = 0): at least 128 query rows per KV head, s2_tile 128 / 256 / 512 and at
+    least 64 (batch, KV head, 128-row tile) workgroups."""
+    rows = cfg.s1 * cfg.nq // cfg.nkv
+    return rows >= 128 and cfg.s2_tile in (128, 256, 512) and cfg.B * cfg.nkv * ((rows + 127) // 128) >= 64
+
+
 def whole_row_path(cfg):
     """Whether the library runs this shape on its whole-row path (the header's rule for
     num_splits = 0): at most 32 query rows per KV head, or more in blocks of 32 with
@@ -355,7 +363,8 @@ def measure_gqa(cfg_id, causal, steps, warmup, rotate, cfg=None):
              "calls_per_s": round(1e3 / region, 1),
              "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gbs / HBM_PEAK_GBS, 4)},
-             "kernel": ("pa::decode_rows_kernel + pa::merge_rows_kernel" if whole_row_path(cfg)
+             "kernel": ("pa::prefill_kernel" if prefill_path(cfg)
+                        else "pa::decode_rows_kernel + pa::merge_rows_kernel" if whole_row_path(cfg)
                         else "pa::decode_kernel")}
     if rows > 32:
         flops = causal_flops(cfg, seqs) if causal else 4 * cfg.D * cfg.s1 * cfg.nq * sum(seqs)

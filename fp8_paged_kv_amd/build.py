@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa_fp8.so")
-SOURCES = ["pa_fp8_decode.hip", "pa_fp8_decode_rows.hip", "pa_fp8_mla.hip", "pa_fp8_cache.hip", "pa_fp8_epilog.hip",
+SOURCES = ["pa_fp8_decode.hip", "pa_fp8_decode_rows.hip", "pa_fp8_prefill.hip", "pa_fp8_mla.hip", "pa_fp8_cache.hip", "pa_fp8_epilog.hip",
            "pa_fp8_api.hip"]
 
 

@@ -107,6 +107,16 @@ bool use_rows_path(int B, int s1, int nq, int nkv, int s2_tile, int num_splits) 
     return num_splits == 0 && pa::rows_path_supported(nkv, s2_tile, s1 * (nq / nkv), s1, nq, B);
 }
 
+// Many query rows per KV head (a prefill chunk, a long multi-token step): the prefill
+// kernel, one workgroup per (batch, KV head, 128 rows) sharing each staged K / V block among
+// its rows, when there are enough such workgroups to occupy the device; not for the debug
+// entry point (it has no dumps).
+bool use_prefill_path(int B, int s1, int nq, int nkv, int s2_tile, int num_splits, bool debug) {
+    const int rows = s1 * (nq / nkv);
+    return num_splits == 0 && !debug && pa::prefill_supported(s2_tile) && rows >= 128 &&
+           (int64_t)B * nkv * pa::prefill_row_tiles(rows) >= 64;
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Zero n int32 words (the per-head path's arrival counters in the scratch array).
@@ -257,7 +267,9 @@ pa_status_t run(const void* q, const float* q_scale, const uint8_t* k_cache, con
         e = hipGetLastError();
         if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
     }
-    if (rows) {
+    if (use_prefill_path(B, s1, nq, nkv, s2_tile, num_splits, debug)) {
+        e = pa::launch_prefill(p, static_cast<hipStream_t>(stream));
+    } else if (rows) {
         if (debug && p.dbg_rows) {
             e = pa::launch_fill_rows(p, static_cast<hipStream_t>(stream));
             if (e != hipSuccess) return fail(PA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));

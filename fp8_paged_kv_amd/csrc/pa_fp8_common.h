@@ -89,6 +89,10 @@ constexpr int kRowsMaxGrid = 256;   // whole-row path: at most one workgroup per
 int rows_group(int nkv);            // KV heads per whole-row workgroup
 int rows_row_blocks(int rows);      // query-row blocks per KV head on the whole-row path
 hipError_t launch_decode_rows(const DecodeParams& p, int cus, hipStream_t stream, bool debug);
+// many query rows per KV head (chunked prefill): one workgroup per (batch, KV head, 128 rows)
+int prefill_row_tiles(int rows);
+bool prefill_supported(int s2_tile);
+hipError_t launch_prefill(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_fill_rows(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace pa

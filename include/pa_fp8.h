@@ -110,7 +110,13 @@ pa_status_t pa_fp8_decode_workspace_size(int B, int s1, int nq, int nkv, int D, 
  * the number of contiguous tile ranges each sequence is split into (>= 1).
  * Whenever pa_fp8_decode_workspace_size reports a nonzero size,
  * workspace_dev must hold at least that many bytes.
- * Two kernels serve the call (same results within the stated tolerance):
+ * Three kernels serve the call (same results within the stated tolerance):
+ *  - num_splits == 0, at least 128 query rows per KV head (s1 * nq / nkv),
+ *    s2_tile 128, 256 or 512 and at least 64 (batch, KV head, 128-row tile)
+ *    workgroups (a prefill chunk, a long multi-token step): one workgroup per
+ *    such tile walks the whole sequence, staging each 128-token K or V block
+ *    once for its 128 rows; no workspace is used (the debug entry point
+ *    takes the whole-row path instead).
  *  - num_splits == 0 and the shape inside the whole-row path's limits: one
  *    workgroup per CU streams a cost-balanced range of (batch, KV-head pair,
  *    block of query rows, tile) units and a small second kernel merges split
@@ -191,10 +197,11 @@ pa_status_t pa_fp8_decode_debug(const void* q_dev, const float* q_scale_dev,
  * be a prefill chunk (hundreds of positions).  Each position keeps its own
  * tiles over [0, n_s) (P quantised per row over the tile's tokens that row
  * sees); n_s = 0 gives a zero row.  Same arguments, workspace, split count
- * and paths as pa_fp8_decode: the whole-row path (query rows in blocks of 32
- * when there are more than 32) when num_splits == 0 and the shape is inside its
- * limits, else the per-head path, which takes any number of query rows per KV
- * head (blocks of 32 rows when there are more than 64).
+ * and paths as pa_fp8_decode: the prefill kernel for 128 or more query rows
+ * per KV head under its conditions, the whole-row path (query rows in blocks
+ * of 32 when there are more than 32) when num_splits == 0 and the shape is
+ * inside its limits, else the per-head path, which takes any number of query
+ * rows per KV head (blocks of 32 rows when there are more than 64).
  */
 pa_status_t pa_fp8_decode_causal(const void* q_dev, const float* q_scale_dev, const uint8_t* k_cache_dev,
                                  const float* k_scale_dev, const uint8_t* v_cache_dev, const float* v_scale_dev,

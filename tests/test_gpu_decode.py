@@ -323,3 +323,34 @@ def test_prefill_causal_poison_bit_identical(B, num_splits):
     clean = _run(B, dict(synth.make_gqa_inputs(cfg), causal=True), num_splits, "prefill poison clean")
     dirty = _run(B, dict(synth.make_gqa_inputs(cfg, poison=True), causal=True), num_splits, "prefill poison dirty")
     assert np.array_equal(clean, dirty)
+
+
+@pytest.mark.parametrize("s1,nq,nkv,s2_tile,seqs,causal", [
+    (128, 32, 4, 128, (100, 700, 1500), True),          # 8 row tiles of 128; seq < s1 in the first
+    (100, 24, 4, 256, (0, 333, 1024, 1900), True),      # 600 rows: a last row tile of 88; an empty sequence
+    (16, 64, 4, 512, (5, 900, 77, 1400, 513, 2048, 0, 1025), False),   # 256 rows, no causal limit
+])
+def test_prefill_kernel_parity(B, oracle_mod, s1, nq, nkv, s2_tile, seqs, causal):
+    """128 or more query rows per KV head and at least 64 (batch, KV head, 128-row)
+    workgroups: the prefill kernel (each K / V block staged and converted once per
+    128 rows).  Against the oracle; positions that see no token give zero rows."""
+    mb = (max(seqs) + 127) // 128 + 1
+    cfg = _case(f"prefill-kernel-s1{s1}-nq{nq}", B=len(seqs), s1=s1, nq=nq, nkv=nkv, s2_tile=s2_tile,
+                seq_lens=seqs, num_blocks=mb * len(seqs), max_blocks_per_seq=mb, seed=110 + s1 + nq)
+    inp = dict(synth.make_gqa_inputs(cfg), causal=causal)
+    ref = oracle_mod.gqa_decode(inp)
+    got = _run(B, inp, 0, f"prefill kernel s1={s1} nq={nq} nkv={nkv} tile={s2_tile} causal={causal}")
+    compare(got, ref, f"prefill kernel s1={s1} nq={nq} nkv={nkv} tile={s2_tile} causal={causal}", max_ulps=16)
+    rows = got.reshape(len(seqs), s1, nq, 128)
+    for bi, sq in enumerate(seqs):
+        nz = max(0, s1 - sq) if causal else (s1 if sq == 0 else 0)
+        assert np.all(rows[bi, :nz] == 0.0)
+
+
+def test_prefill_kernel_poison_bit_identical(B):
+    """The prefill kernel: NaN codes and scales past every sequence change no output bit."""
+    cfg = _case("prefill-kernel-poison", B=3, s1=64, nq=64, nkv=8, s2_tile=256, seq_lens=(40, 700, 1300),
+                num_blocks=30, max_blocks_per_seq=11, seed=93)
+    clean = _run(B, dict(synth.make_gqa_inputs(cfg), causal=True), 0, "prefill kernel poison clean")
+    dirty = _run(B, dict(synth.make_gqa_inputs(cfg, poison=True), causal=True), 0, "prefill kernel poison dirty")
+    assert np.array_equal(clean, dirty)
