@@ -132,6 +132,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
     const bool row_ok = ra < rows;
     const int s_of = row_ok ? ra / a.G : 0;
     const int lim = row_ok ? seq - (a.causal ? a.s1 - 1 - s_of : 0) : 0;   // tokens this row sees
+    // tokens every row of this wave sees: its first row's (limits grow with the row), 0 if the
+    // wave holds rows past the end
+    const int wave_lim = (kRowsPerWg * rt + 16 * w + 15 < rows) ? __builtin_amdgcn_readfirstlane(lim) : 0;
     // tokens any row of the workgroup sees (rows grow with s, so the last valid row sees most)
     const int ra_last = min(kRowsPerWg * rt + kRowsPerWg, rows) - 1;
     const int wg_lim = seq - (a.causal ? a.s1 - 1 - ra_last / a.G : 0);
@@ -262,11 +265,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
     // barrier then also ends every wave's use of the BF16 copy (k + 1) % 2 and of ring slot
     // k % NST; refill that slot with step k + NST and convert step k + 1 while this step multiplies.
     int gs = 0;
+    // Waves 0-3 multiply first and convert after, waves 4-7 the other way round: each SIMD holds
+    // one wave of each half, so the conversions' VALU work overlaps the other wave's MFMAs.
+    const bool convert_first = w >= 4;
     auto step_begin = [&]() {
         if (gs + 1 < nsteps) wait_loads(gs + 1, gs + NST - 1);
         pf_barrier();
         if (gs + NST < nsteps) issue(gs + NST);
-        if (gs + 1 < nsteps) convert(gs + 1);
+        if (convert_first && gs + 1 < nsteps) convert(gs + 1);
+    };
+    auto step_end = [&]() {
+        if (!convert_first && gs + 1 < nsteps) convert(gs + 1);
+        ++gs;
     };
 
     if (nsteps > 0) {
@@ -312,13 +322,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) sv[q][4 * k + i] = acc[i] * kk[i] * qcoef;
                     }
+                    if (p0 + 32 > wave_lim) {                      // some row of the wave stops in this chunk
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        sv[q][j] = (p0 + chunk_token(lg, j) < lim) ? sv[q][j] : -INFINITY;
-                        rmax = fmaxf(rmax, sv[q][j]);
+                        for (int j = 0; j < 8; ++j) sv[q][j] = (p0 + chunk_token(lg, j) < lim) ? sv[q][j] : -INFINITY;
                     }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) rmax = fmaxf(rmax, sv[q][j]);
                 }
-                ++gs;
+                step_end();
             } else {
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc)
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
                         O[c] = mfma_bf16(pop, vop, O[c]);
                     }
                 }
-                ++gs;
+                step_end();
             }
         }
         // ---------------- finish the rescale, update the running state ---------------------------
