@@ -41,13 +41,14 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
-    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma", "phases", "valu-rates"],
+    ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma", "phases", "valu-rates",
+                                     "prefill"],
                     default="decode",
                     help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
                          "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows; "
                          "ceiling: read-only probes of config 1's paged access pattern and of a contiguous "
                          "buffer, beside the decode; valu-rates: issue rate of the FP8 dequantisation "
-                         "instructions")
+                         "instructions; prefill: the causal prefill chunk alone")
     ap.add_argument("--no-secondary", action="store_true",
                     help="headline only: skip the other workloads' entries")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -190,6 +191,10 @@ def main():
         return run_phases(args)
     if args.op == "valu-rates":
         return run_valu_rates(args)
+    if args.op == "prefill":
+        print(json.dumps(measure_gqa(None, True, args.steps, args.warmup, max(1, args.rotate), cfg=prefill_config())),
+              flush=True)
+        return
     if args.config == 4:
         return run_mla(args)
     cfg = synth.CONFIGS[args.config]
