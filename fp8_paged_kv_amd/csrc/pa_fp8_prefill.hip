@@ -89,7 +89,7 @@ template <int NBLK>
 __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
     constexpr int T = NBLK * kBlock;          // s2_tile
     constexpr int NQ = T / 32;                // 32-token chunks of a tile
-    constexpr int NST = 3;                    // staging ring of FP8 blocks: NST - 1 in flight (5 was slower)
+    constexpr int NST = 3;                    // staging ring of FP8 blocks: NST - 1 in flight (4 and 5 were slower)
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[NST][kBlock * kHeadDim];
     __shared__ __attribute__((aligned(16))) float s_ks[NST][kBlock];
     // BF16 copies, double-buffered: K [token][dim] or V [channel][slot]; and the K block's scales
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
             s_order[rank] = i;
         }
         __syncthreads();
-        b = s_order[bo];
+        b = __builtin_amdgcn_readfirstlane(s_order[bo]);
     }
     int seq = a.seqs[b];
     seq = seq < 0 ? 0 : (seq > a.capacity ? a.capacity : seq);
@@ -185,7 +185,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
         int blk;
         bool is_v;
         step_of(k, blk, is_v);
-        int id = table[blk];
+        // a scalar load: a vector one would share vmcnt with the ring's loads and, waited for
+        // before the addresses it feeds, drain every block in flight
+        int id = ((const __attribute__((address_space(4))) int32_t*)table)[blk];
         id = (id < 0 || id >= a.num_blocks) ? 0 : id;
         const uint8_t* base = (is_v ? a.v_cache : a.k_cache) + ((int64_t)id * kBlock * a.nkv + h) * kHeadDim;
         uint8_t* st = s_stage[k % NST];
