@@ -42,13 +42,14 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id (1-3 GQA, 4 MLA)")
     ap.add_argument("--op", choices=["decode", "scatter", "epilog", "ceiling", "fp8-mfma", "phases", "valu-rates",
-                                     "prefill"],
+                                     "prefill", "lds-patterns"],
                     default="decode",
                     help="scatter: the FP8 KV-cache writer filling config 1's pool (prefill-sized write); "
                          "epilog: KvCompressEpilog mode 1 on 131072 MLA-latent rows; "
                          "ceiling: read-only probes of config 1's paged access pattern and of a contiguous "
                          "buffer, beside the decode; valu-rates: issue rate of the FP8 dequantisation "
-                         "instructions; prefill: the causal prefill chunk alone")
+                         "instructions; prefill: the causal prefill chunk alone; lds-patterns: LDS read rate "
+                         "of lane address patterns")
     ap.add_argument("--no-secondary", action="store_true",
                     help="headline only: skip the other workloads' entries")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -191,6 +192,8 @@ def main():
         return run_phases(args)
     if args.op == "valu-rates":
         return run_valu_rates(args)
+    if args.op == "lds-patterns":
+        return run_lds_patterns(args)
     if args.op == "prefill":
         print(json.dumps(measure_gqa(None, True, args.steps, args.warmup, max(1, args.rotate), cfg=prefill_config())),
               flush=True)
@@ -544,6 +547,47 @@ def run_valu_rates(args):
         res[name]["relative_to_v_mul_f32"] = round(res[name]["ns_per_wave_instruction_per_simd"] / base, 2)
     print(json.dumps({"metric": "VALU issue rate, wave64 instructions", "simds": simds,
                       "waves_per_simd": grid * (threads // 64) / simds, "rates": res}), flush=True)
+
+
+def run_lds_patterns(args):
+    """LDS read rate of lane address patterns, from the probe library: 2 workgroups of
+    8 waves per CU, each wave issuing iters x 8 independent reads; event-timed.  Bytes
+    per cycle per CU at 2.4 GHz; a pattern whose lanes collide in banks reads slower."""
+    import ctypes
+    import torch
+    from fp8_paged_kv_amd import build
+    P = ctypes.CDLL(build.PROBE_LIB)
+    P.pa_probe_lds_pattern.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+    P.pa_probe_lds_pattern.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid, iters = 2 * cus, 2048
+    sink = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cases = [(0, 0, 16), (0, 0, 8)]
+    cases += [(1, s, 16) for s in (256, 264, 272, 288, 320, 384, 512)]
+    cases += [(2, s, 16) for s in (128, 136, 256, 272)]
+    cases += [(3, s, 16) for s in (16, 32, 64, 128, 136, 144, 272)]
+    cases += [(3, s, 8) for s in (8, 16, 128, 136)]
+    names = {0: "16 lane", 1: "(lane % 16) stride + 16 (lane / 16)", 2: "(lane / 4) stride + 16 (lane % 4)",
+             3: "lane stride"}
+    rows = []
+    for pat, stride, width in cases:
+        for _ in range(2):
+            if P.pa_probe_lds_pattern(pat, stride, width, grid, iters, sink.data_ptr(), st) != 0:
+                sys.exit(f"probe launch failed for pattern {pat} stride {stride}")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            P.pa_probe_lds_pattern(pat, stride, width, grid, iters, sink.data_ptr(), st)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        nbytes = grid * 8 * iters * 8 * 64 * width
+        rows.append({"pattern": names[pat].replace("16", str(width)) if pat == 0 else names[pat], "stride": stride,
+                     "bytes_per_lane": width, "bytes_per_clk_per_cu": round(nbytes / t / cus / 2.4e9, 1)})
+    print(json.dumps({"metric": "LDS read rate by lane address pattern", "cus": cus, "rows": rows}), flush=True)
 
 
 def run_fp8_mfma(args):

@@ -80,8 +80,20 @@ __device__ __forceinline__ i32x2p pf_read_tr8(const uint8_t* p) {
 }
 
 constexpr int kRowsPerWg = 128;              // query rows of a KV head per workgroup
-constexpr int kBf16Stride = 272;             // bytes per token (K) or channel (V) row of the BF16 copy
+// Row r of the BF16 copy (a K token or a V channel, 256 bytes) starts at byte
+// 288 r + 16 ((r / 16) % 2).  gfx950 serves a 16-byte LDS read or write 32 lanes at a time over
+// 128 four-byte banks: with this layout the MFMA operand reads (16 rows x 2 pieces) and the
+// conversions' writes (32 rows x 1 piece) each cover all 128 banks once.  (With rows 272 bytes
+// apart the operand reads took two passes.)
+constexpr int kBf16Stride = 288;
+__device__ __forceinline__ int pf_row(int r) { return kBf16Stride * r + 16 * ((r >> 4) & 1); }
 constexpr int kOrderMax = 256;               // batches ordered by length (longest first) up to this count
+
+// Staged FP8 rows are 128 bytes (eight 16-byte pieces), so every token row starts in the same
+// LDS bank; piece p of token t is stored in slot p ^ pf_swz(t).  With this swizzle the
+// conversions' reads (a token's pieces across the lanes of a K read, eight tokens' same piece
+// across the lanes of a transposing V read) fall in distinct banks.
+__device__ __forceinline__ int pf_swz(int t) { return (t ^ (t >> 1) ^ (t >> 2)) & 7; }
 
 }  // namespace
 
@@ -194,8 +206,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
             const int i = 2 * w + d;                          // tokens 8 i .. 8 i + 7
-            const int tok = 8 * i + (lane >> 3);
-            pf_dma16(base + (int64_t)tok * a.nkv * kHeadDim + 16 * (lane & 7), (lds_ptr_p)(st + 1024 * i));
+            const int tok = 8 * i + (lane >> 3);              // slot lane % 8 of its row
+            pf_dma16(base + (int64_t)tok * a.nkv * kHeadDim + 16 * ((lane & 7) ^ pf_swz(tok)), (lds_ptr_p)(st + 1024 * i));
         }
         if (!is_v && w < 2) {
             const int tok = 64 * w + lane;
@@ -223,11 +235,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
         const uint8_t* st = s_stage[k % NST];
         uint8_t* bf = s_bf[k & 1];
         if (!is_v) {
-            // K codes -> BF16 [token][dim]: thread i takes token i / 4, dims 32 (i % 4) .. + 32
-            const int tok = threadIdx.x >> 2, d0 = 32 * (threadIdx.x & 3);
-            const i32x4 c0 = *reinterpret_cast<const i32x4*>(st + tok * kHeadDim + d0);
-            const i32x4 c1 = *reinterpret_cast<const i32x4*>(st + tok * kHeadDim + d0 + 16);
-            uint8_t* dst = bf + tok * kBf16Stride + 2 * d0;
+            // K codes -> BF16 [token][dim]: thread i takes token i % 128, dims 32 (i / 128) .. + 32
+            // (pieces 2 (i / 128) and 2 (i / 128) + 1)
+            const int tok = threadIdx.x & 127, qd = threadIdx.x >> 7, sw = pf_swz(tok);
+            const i32x4 c0 = *reinterpret_cast<const i32x4*>(st + tok * kHeadDim + 16 * ((2 * qd) ^ sw));
+            const i32x4 c1 = *reinterpret_cast<const i32x4*>(st + tok * kHeadDim + 16 * ((2 * qd + 1) ^ sw));
+            uint8_t* dst = bf + pf_row(tok) + 64 * qd;
             *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_op((uint32_t)c0[0], (uint32_t)c0[1]);
             *reinterpret_cast<bf16x8*>(dst + 16) = fp8x8_to_op((uint32_t)c0[2], (uint32_t)c0[3]);
             *reinterpret_cast<bf16x8*>(dst + 32) = fp8x8_to_op((uint32_t)c1[0], (uint32_t)c1[1]);
@@ -245,7 +258,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
                 const int cq = combo >> 5, sg = (combo >> 3) & 3, cb = combo & 7;
                 const int jj = (lane & 15) >> 1, hh = lane & 1;
                 const int tok = 32 * cq + chunk_token(sg, jj);
-                const i32x2p x = pf_read_tr8(st + tok * kHeadDim + 16 * cb + 8 * hh);
+                const i32x2p x = pf_read_tr8(st + tok * kHeadDim + 16 * (cb ^ pf_swz(tok)) + 8 * hh);
                 uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1];
                 if (p0blk + 32 * cq + 32 > seq) {
                     // tokens past the sequence (their codes may be NaN) contribute exact zeros
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
                     x1 &= m1;
                 }
                 const int ch = 16 * cb + (lane & 15);
-                *reinterpret_cast<bf16x8*>(bf + ch * kBf16Stride + 2 * (32 * cq + 8 * sg)) = fp8x8_to_op(x0, x1);
+                *reinterpret_cast<bf16x8*>(bf + pf_row(ch) + 2 * (32 * cq + 8 * sg)) = fp8x8_to_op(x0, x1);
             }
         }
     };
@@ -316,7 +329,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int ks = 0; ks < 4; ++ks) {
-                            const bf16x8 kop = *reinterpret_cast<const bf16x8*>(bf + (tb + lr) * kBf16Stride +
+                            const bf16x8 kop = *reinterpret_cast<const bf16x8*>(bf + pf_row(tb + lr) +
                                                                                2 * (32 * ks + 8 * lg));
                             acc = mfma_bf16(kop, qop[ks], acc);
                         }
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
                     const bf16x8 pop = fp8x8_to_op(p8[q][0], p8[q][1]);
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
-                        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(bf + (16 * c + lr) * kBf16Stride +
+                        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(bf + pf_row(16 * c + lr) +
                                                                            2 * (32 * cc + 8 * lg));
                         O[c] = mfma_bf16(pop, vop, O[c]);
                     }

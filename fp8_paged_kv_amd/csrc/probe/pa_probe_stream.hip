@@ -12,8 +12,8 @@
 //    dispatcher balancing the load;
 //  * probe_contiguous_kernel: a plain contiguous read of a buffer with 16-byte
 //    loads, grid-strided.
-// Beside them: the FP8 MFMA against exact sums, and the issue rate of the VALU
-// instructions that dequantise FP8 codes.
+// Beside them: the FP8 MFMA against exact sums, the issue rate of the VALU
+// instructions that dequantise FP8 codes, and the LDS read rate of lane address patterns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -210,9 +210,64 @@ __global__ void probe_valu_rate_kernel(int iters, float* sink) {
     sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// LDS read-rate probe: each lane reads WIDTH bytes (ds_read_b128 or ds_read_b64) at byte
+// address base(lane) + 4096 u + 256 (it % 16) of a 64 KB LDS buffer, u = 0..7 per iteration
+// (offsets that are multiples of 256 bytes keep every lane in the same bank).  base(lane),
+// lane = 16 g + r: pattern 0: WIDTH lane (contiguous); 1: r stride + WIDTH g (sixteen rows,
+// four pieces each: an MFMA operand read from a row-major tile); 2: (lane / 4) stride +
+// WIDTH (lane % 4); 3: lane stride.  The host keeps base(lane) <= 32768 - WIDTH.
+template <int WIDTH>
+__global__ __launch_bounds__(512) void probe_lds_kernel(int pattern, int stride, int iters, uint32_t* sink) {
+    __shared__ __attribute__((aligned(16))) uint32_t buf[16384];
+    for (int i = threadIdx.x; i < 16384; i += blockDim.x) buf[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    int base;
+    if (pattern == 0) base = WIDTH * lane;
+    else if (pattern == 1) base = r * stride + WIDTH * g;
+    else if (pattern == 2) base = (lane >> 2) * stride + WIDTH * (lane & 3);
+    else base = lane * stride;
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(buf) + base;
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+        const uint8_t* q = p + 256 * (it & 15);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (WIDTH == 16) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(q + 4096 * u);
+                acc ^= v[0] ^ v[3];
+            } else {
+                typedef int i32x2 __attribute__((ext_vector_type(2)));
+                const i32x2 v = *reinterpret_cast<const i32x2*>(q + 4096 * u);
+                acc ^= (uint32_t)(v[0] ^ v[1]);
+            }
+        }
+    }
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// LDS read-pattern probe (see probe_lds_kernel): `grid` workgroups of 512 threads, width 8
+// or 16 bytes per lane.  sink: grid * 512 words.  Returns 0 or a hipError_t (invalid value
+// when a lane's address would leave the buffer).
+int pa_probe_lds_pattern(int pattern, int stride, int width, int grid, int iters, uint32_t* sink, void* stream) {
+    if (grid <= 0 || iters <= 0 || pattern < 0 || pattern > 3 || stride < 0 || (width != 8 && width != 16))
+        return (int)hipErrorInvalidValue;
+    const int64_t top = pattern == 0 ? (int64_t)width * 63
+                      : pattern == 1 ? (int64_t)15 * stride + width * 3
+                      : pattern == 2 ? (int64_t)15 * stride + width * 3
+                      : (int64_t)63 * stride;
+    if (top > 32768 - width || (stride % 8) != 0) return (int)hipErrorInvalidValue;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (width == 16)
+        hipLaunchKernelGGL(probe_lds_kernel<16>, dim3(grid), dim3(512), 0, st, pattern, stride, iters, sink);
+    else
+        hipLaunchKernelGGL(probe_lds_kernel<8>, dim3(grid), dim3(512), 0, st, pattern, stride, iters, sink);
+    return (int)hipGetLastError();
+}
 
 // VALU issue-rate probe: `grid` workgroups of `threads` threads (a multiple of 64, at
 // most 1024), each wave running iters x 8 instructions of kind `op` (see
