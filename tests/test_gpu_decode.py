@@ -347,6 +347,20 @@ def test_prefill_kernel_parity(B, oracle_mod, s1, nq, nkv, s2_tile, seqs, causal
         assert np.all(rows[bi, :nz] == 0.0)
 
 
+def test_prefill_kernel_many_batches(B, oracle_mod):
+    """More batches than the prefill kernel orders by length (300 > 256): workgroups take
+    the batches in index order.  s1=16, G=8 (128 query rows per KV head), lengths from 0
+    to 899 (some shorter than s1), causal; against the oracle."""
+    seqs = tuple((37 * i + (i * i) % 11) % 900 for i in range(300))
+    mb = (max(seqs) + 127) // 128 + 1
+    cfg = _case("prefill-kernel-b300", B=len(seqs), s1=16, nq=8, nkv=1, s2_tile=256, seq_lens=seqs,
+                num_blocks=mb * len(seqs), max_blocks_per_seq=mb, seed=131)
+    inp = dict(synth.make_gqa_inputs(cfg), causal=True)
+    ref = oracle_mod.gqa_decode(inp)
+    got = _run(B, inp, 0, "prefill kernel B=300 s1=16 nq=8 nkv=1 tile=256 causal")
+    compare(got, ref, "prefill kernel B=300", max_ulps=16)
+
+
 def test_prefill_kernel_poison_bit_identical(B):
     """The prefill kernel: NaN codes and scales past every sequence change no output bit."""
     cfg = _case("prefill-kernel-poison", B=3, s1=64, nq=64, nkv=8, s2_tile=256, seq_lens=(40, 700, 1300),
