@@ -101,7 +101,7 @@ template <int NBLK>
 __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
     constexpr int T = NBLK * kBlock;          // s2_tile
     constexpr int NQ = T / 32;                // 32-token chunks of a tile
-    constexpr int NST = 3;                    // staging ring of FP8 blocks: NST - 1 in flight (4 and 5 were slower)
+    constexpr int NST = 2;                    // staging ring of FP8 blocks: one in flight (3, 4, 5 were slower)
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[NST][kBlock * kHeadDim];
     __shared__ __attribute__((aligned(16))) float s_ks[NST][kBlock];
     // BF16 copies, double-buffered: K [token][dim] or V [channel][slot]; and the K block's scales
@@ -278,19 +278,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
     };
     // Step k: its BF16 copy was made during step k - 1.  Wait for the loads of step k + 1; the
     // barrier then also ends every wave's use of the BF16 copy (k + 1) % 2 and of ring slot
-    // k % NST; refill that slot with step k + NST and convert step k + 1 while this step multiplies.
+    // k % NST; refill that slot with step k + NST, multiply step k, then convert step k + 1.
+    // (Half the waves converting before they multiply, so that each SIMD overlaps one wave's
+    // conversion with the other's MFMAs, was 8 % slower once the LDS accesses were
+    // conflict-free.)
     int gs = 0;
-    // Waves 0-3 multiply first and convert after, waves 4-7 the other way round: each SIMD holds
-    // one wave of each half, so the conversions' VALU work overlaps the other wave's MFMAs.
-    const bool convert_first = w >= 4;
     auto step_begin = [&]() {
         if (gs + 1 < nsteps) wait_loads(gs + 1, gs + NST - 1);
         pf_barrier();
         if (gs + NST < nsteps) issue(gs + NST);
-        if (convert_first && gs + 1 < nsteps) convert(gs + 1);
     };
     auto step_end = [&]() {
-        if (!convert_first && gs + 1 < nsteps) convert(gs + 1);
+        if (gs + 1 < nsteps) convert(gs + 1);
         ++gs;
     };
 
