@@ -321,7 +321,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {                  // 32-token chunks of the block
                     const int q = 4 * r + cc;
-                    const int p0 = p0blk + 32 * cc;
 #pragma unroll
                     for (int k = 0; k < 2; ++k) {
                         const int tb = 32 * cc + 16 * k;          // 16-token block
@@ -336,13 +335,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) sv[q][4 * k + i] = acc[i] * kk[i] * qcoef;
                     }
-                    if (p0 + 32 > wave_lim) {                      // some row of the wave stops in this chunk
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) sv[q][j] = (p0 + chunk_token(lg, j) < lim) ? sv[q][j] : -INFINITY;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) rmax = fmaxf(rmax, sv[q][j]);
                 }
+                if (p0blk + kBlock > wave_lim) {                   // some row of the wave stops in this block
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            sv[4 * r + cc][j] = (p0blk + 32 * cc + chunk_token(lg, j) < lim) ? sv[4 * r + cc][j] : -INFINITY;
+                }
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) rmax = fmaxf(rmax, sv[4 * r + cc][j]);
                 step_end();
             } else {
 #pragma unroll
