@@ -214,3 +214,25 @@ def test_noalloc_host_validation_codes(lib, over, code):
     assert len(msg) > 0
     if code == 4:
         assert b"scratch" in msg
+
+
+def test_lds_probe_rejects_out_of_range_patterns():
+    """The LDS read-pattern probe (a measurement tool beside the library) checks on the
+    host that every lane's address stays inside its 64 KB buffer: a stride that would
+    leave it, a stride not a multiple of 8, a bad width or pattern returns
+    hipErrorInvalidValue (1) before anything is launched."""
+    from fp8_paged_kv_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        build.build_probe()
+    P = ctypes.CDLL(build.PROBE_LIB)
+    P.pa_probe_lds_pattern.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+    P.pa_probe_lds_pattern.restype = ctypes.c_int
+    bad = [(3, 528, 16),     # 63 lanes x 528 bytes > 32 KB base range
+           (1, 2200, 16),    # 15 rows x 2200 bytes
+           (1, 272, 12),     # width neither 8 nor 16
+           (4, 16, 16),      # no such pattern
+           (1, 270, 16),     # stride not a multiple of 8
+           (0, 0, 0)]
+    for pat, stride, width in bad:
+        assert P.pa_probe_lds_pattern(pat, stride, width, 512, 16, None, None) == 1, (pat, stride, width)
+    assert P.pa_probe_lds_pattern(0, 0, 16, 0, 16, None, None) == 1          # empty grid
