@@ -1,8 +1,8 @@
 """The decode calls captured in a HIP graph (torch.cuda.CUDAGraph on ROCm):
 every replay, with eager calls and synchronisations between replays, gives
 the eager result bit for bit — the whole-row path (its per-call partition), the
-per-head path with splits (its arrival counters, left at zero by every call)
-and the MLA decode.  Workspaces and outputs are allocated before capture; the
+per-head path with splits (its arrival counters, left at zero by every call),
+the prefill kernel and the MLA decode.  Workspaces and outputs are allocated before capture; the
 calls enqueue kernels only.  Every test prints its case first."""
 from __future__ import annotations
 
@@ -71,6 +71,33 @@ def test_gqa_decode_graph_replays(B, num_splits):
             B.decode_inputs(inp, num_splits=num_splits, out=o, workspace=ws, stream=st)
 
     _check_replays(run_eager, run_into, outs, f"gqa splits={num_splits}")
+
+
+def test_prefill_kernel_graph_replays(B):
+    """A causal prefill chunk on the prefill kernel (1024 query rows per KV head, 64
+    workgroups): its in-kernel batch ordering and staging replay bit for bit."""
+    cfg = synth.GqaConfig(name="graph-prefill", B=8, s1=64, nq=16, nkv=1,
+                          seq_lens=(70, 300, 1100, 2500, 64, 900, 1700, 0), s2_tile=256,
+                          num_blocks=8 * 21, max_blocks_per_seq=21, seed=37)
+    sets = [dict(synth.make_gqa_inputs(cfg, device="cuda", seed=37 + i), causal=True) for i in range(2)]
+    print("[gpu] graph replays, prefill kernel, B=8 s1=64 nq=16 nkv=1 causal", flush=True)
+    need, _ = B.workspace_size(cfg.B, cfg.s1, cfg.nq, cfg.nkv, cfg.D, cfg.block_size, cfg.max_blocks_per_seq,
+                               cfg.s2_tile, 0)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    shape = (cfg.B * cfg.s1, cfg.nq, cfg.D)
+    outs = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in sets]
+    eager_out = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in sets]
+
+    def run_eager(st):
+        for inp, o in zip(sets, eager_out):
+            B.decode_inputs(inp, num_splits=0, out=o, workspace=ws, stream=st)
+        return eager_out
+
+    def run_into(st):
+        for inp, o in zip(sets, outs):
+            B.decode_inputs(inp, num_splits=0, out=o, workspace=ws, stream=st)
+
+    _check_replays(run_eager, run_into, outs, "prefill kernel")
 
 
 @pytest.mark.parametrize("nq,s2_tile", [(32, 256), (64, 512)])
