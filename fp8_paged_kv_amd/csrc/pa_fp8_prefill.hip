@@ -150,29 +150,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
     // tokens any row of the workgroup sees (rows grow with s, so the last valid row sees most)
     const int ra_last = min(kRowsPerWg * rt + kRowsPerWg, rows) - 1;
     const int wg_lim = seq - (a.causal ? a.s1 - 1 - ra_last / a.G : 0);
-    bf16x8 qop[4];
-    float qcoef = 0.f;
-    {
-        uint32_t wds[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-        if (row_ok) {
-            const int64_t qrow = ((int64_t)b * a.s1 + s_of) * a.nq + h * a.G + (ra - s_of * a.G);
-            const float qs = a.q_scale[qrow];
-            qcoef = qs * a.softmax_scale * kLog2e;
-            const QRecip d = q_recip(qs);
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                // dims 32 ks + 8 lg + [0, 8) for ks = 2 half, 2 half + 1
-                const uint16_t* qp = a.q + qrow * kHeadDim + 64 * half + 8 * lg;
-                const i32x4 v0 = *reinterpret_cast<const i32x4*>(qp);
-                const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + 32);
-                const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
-                                         (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
-                quantise_q16(raw, d, wds[half]);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qop[ks] = fp8x8_to_op(wds[ks >> 1][2 * (ks & 1)], wds[ks >> 1][2 * (ks & 1) + 1]);
-    }
 
     const int nblocks = wg_lim <= 0 ? 0 : (wg_lim + kBlock - 1) / kBlock;   // blocks any row needs
     const int ntiles = (nblocks + NBLK - 1) / NBLK;
@@ -293,8 +270,33 @@ __global__ __launch_bounds__(512) void prefill_kernel(DecodeParams a) {
         ++gs;
     };
 
+    // the first blocks' loads go out before the query rows are staged, so that the two
+    // latencies overlap
+    for (int k = 0; k < NST && k < nsteps; ++k) issue(k);       // one step per ring slot
+    bf16x8 qop[4];
+    float qcoef = 0.f;
+    {
+        uint32_t wds[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+        if (row_ok) {
+            const int64_t qrow = ((int64_t)b * a.s1 + s_of) * a.nq + h * a.G + (ra - s_of * a.G);
+            const float qs = a.q_scale[qrow];
+            qcoef = qs * a.softmax_scale * kLog2e;
+            const QRecip d = q_recip(qs);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                // dims 32 ks + 8 lg + [0, 8) for ks = 2 half, 2 half + 1
+                const uint16_t* qp = a.q + qrow * kHeadDim + 64 * half + 8 * lg;
+                const i32x4 v0 = *reinterpret_cast<const i32x4*>(qp);
+                const i32x4 v1 = *reinterpret_cast<const i32x4*>(qp + 32);
+                const uint32_t raw[8] = {(uint32_t)v0[0], (uint32_t)v0[1], (uint32_t)v0[2], (uint32_t)v0[3],
+                                         (uint32_t)v1[0], (uint32_t)v1[1], (uint32_t)v1[2], (uint32_t)v1[3]};
+                quantise_q16(raw, d, wds[half]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qop[ks] = fp8x8_to_op(wds[ks >> 1][2 * (ks & 1)], wds[ks >> 1][2 * (ks & 1) + 1]);
+    }
     if (nsteps > 0) {
-        for (int k = 0; k < NST && k < nsteps; ++k) issue(k);   // one step per ring slot
         wait_loads(0, NST - 1);
         pf_barrier();
         convert(0);
